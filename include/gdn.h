@@ -1,0 +1,131 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunk-parallel gated delta-rule prefill.
+ *
+ * The operation (per sequence n and value head h, tokens t in order; K-first
+ * state H in R^{dk x dv}):
+ *
+ *     H_t = (I - beta_t k_t k_t^T) D_t H_{t-1} + beta_t k_t v_t^T,   o_t = H_t^T q_t
+ *
+ * with D_t = exp(g_t) I (per-head gate) or diag(exp(g_t[c])) (per-key-channel
+ * gate), i.e. S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T with S = H^T.
+ * It is the gated-delta-net recurrence of the stratat.com page "hip:
+ * chunk-parallel GDN recurrence (WY form), two parity-gated arms" (section
+ * "What this is"), evaluated chunkwise as that page and the ROCm/rocm-libraries
+ * KDA chunkwise page (section "Summary") describe: per chunk one unit-lower-
+ * triangular solve plus GEMM-shaped folds, then a serial state recurrence.
+ * The argument contract (K-first state, precomputed beta and natural-log g,
+ * explicit grouped heads, immutable h0, separate next state, sticky numerical
+ * status, explicit refusal of unsupported inputs) follows the logismos issue
+ * #46 page ("Verified implementation boundary", "Remaining work",
+ * "Acceptance", and the Sep 6 / Sep 8 activity).
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *     allocates and frees nothing and keeps no global state.
+ *   - Tensors are dense, row-major, last dimension contiguous, no padding.
+ *   - Host-detected errors return synchronously and launch nothing.
+ *   - gdn_chunk_fwd is asynchronous on `stream`; device-detected conditions are
+ *     OR-ed into *status (sticky), which the caller reads after synchronising.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+/* Host return codes. */
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_E_NULL = 1,        /* a required pointer is NULL */
+  GDN_E_SHAPE = 2,       /* sizes negative or inconsistent */
+  GDN_E_UNSUPPORTED = 3, /* outside the supported domain (widths, chunk, dtype, alignment) */
+  GDN_E_ALIAS = 4,       /* an output overlaps an input or another output */
+  GDN_E_WORKSPACE = 5,   /* workspace smaller than gdn_workspace_bytes() or misaligned */
+  GDN_E_LAUNCH = 6       /* the HIP runtime refused a launch */
+} gdn_status;
+
+/* Device status bits, OR-accumulated into *status.  When any bit is set the
+ * contents of o and hT are unspecified; inputs are never modified. */
+#define GDN_ST_NONFINITE_INPUT 0x1u  /* NaN/Inf in q, k, v, g, beta or h0 */
+#define GDN_ST_GATE_DOMAIN 0x2u      /* g > 0, or a per-channel gate below -5 */
+#define GDN_ST_BAD_SEQLENS 0x4u      /* cu_seqlens not 0 = c_0 <= ... <= c_n = total_tokens */
+#define GDN_ST_NONFINITE_OUTPUT 0x8u /* a NaN/Inf was produced in o or hT */
+
+enum { GDN_GATE_HEAD = 0, GDN_GATE_KEY_CHANNEL = 1 };
+enum { GDN_BF16 = 0, GDN_F32 = 1 };
+/* Arithmetic arm: bf16 MFMA operands with fp32 accumulation, or fp32 MFMA
+ * operands (the fp32-fold debug arm).  The state is fp32 in both. */
+enum { GDN_ARM_MFMA_BF16 = 0, GDN_ARM_FOLD_F32 = 1 };
+/* Kernel composition: split (sequence-parallel prep, then scan) or fused
+ * (one kernel computes the chunk tiles and runs the scan).  AUTO picks the
+ * measured default for the problem. */
+enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2 };
+
+typedef struct gdn_problem {
+  int32_t n_seq;        /* number of sequences, >= 0 */
+  int64_t total_tokens; /* packed token count, >= 0 */
+  int32_t seq_len;      /* fixed-length batches: tokens per sequence (total = n_seq*seq_len);
+                           0 when cu_seqlens describes the sequences */
+  int32_t hk;           /* key/query heads, >= 1 */
+  int32_t hv;           /* value heads, a multiple of hk; value head j reads key head j/(hv/hk) */
+  int32_t dk;           /* key width: 32, 64 or 128 */
+  int32_t dv;           /* value width: 32, 64 or 128 */
+  int32_t gate;         /* GDN_GATE_HEAD: g[tok][hv];  GDN_GATE_KEY_CHANNEL: g[tok][hv][dk] */
+  int32_t chunk;        /* 0 = library choice, else 32 or 64 (per-channel gate: 32 only) */
+  int32_t qkv_dtype;    /* GDN_BF16 or GDN_F32 for q, k, v */
+  int32_t o_dtype;      /* GDN_BF16 or GDN_F32 for o */
+  int32_t arm;          /* GDN_ARM_MFMA_BF16 or GDN_ARM_FOLD_F32 */
+  int32_t compose;      /* GDN_COMPOSE_* */
+} gdn_problem;
+
+/* Checks a problem description on the host (no device work).  Returns GDN_OK,
+ * GDN_E_NULL, GDN_E_SHAPE or GDN_E_UNSUPPORTED. */
+gdn_status gdn_validate(const gdn_problem* p);
+
+/* Bytes of device workspace gdn_chunk_fwd needs for *p (written to *bytes).
+ * Same return codes as gdn_validate. */
+gdn_status gdn_workspace_bytes(const gdn_problem* p, size_t* bytes);
+
+/*
+ * gdn_chunk_fwd -- chunkwise gated delta-rule prefill.
+ *   q, k        [total_tokens][hk][dk]   qkv_dtype, 16-byte aligned
+ *   v           [total_tokens][hv][dv]   qkv_dtype, 16-byte aligned
+ *   g           fp32 natural-log decay, [total_tokens][hv] or [total_tokens][hv][dk]
+ *   beta        fp32 [total_tokens][hv]
+ *   h0          fp32 [n_seq][hv][dk][dv] initial states, or NULL for zeros; never written
+ *   cu_seqlens  int32 [n_seq+1] token offsets (0, ..., total_tokens), or NULL for a
+ *               fixed-length batch of n_seq sequences of seq_len tokens; a sequence's
+ *               state starts at its own h0 and chunks never cross a boundary
+ *   o           [total_tokens][hv][dv] o_dtype, 16-byte aligned
+ *   hT          fp32 [n_seq][hv][dk][dv] final states, or NULL; must not overlap h0
+ *   status      one uint32 on the device, zeroed by the caller; device bits OR-ed in
+ *   workspace   device scratch of at least gdn_workspace_bytes() bytes, 256-byte aligned;
+ *               its contents are undefined before and after the call
+ *   stream      a hipStream_t (NULL = the default stream)
+ * Returns GDN_OK after enqueueing every kernel, or a host error with nothing launched.
+ */
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* h0,
+                         const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a host return code. */
+const char* gdn_error_string(int32_t code);
+
+/* Text naming the device status bits set in `bits` ("ok" when none).  The
+ * returned pointer refers to thread-local storage valid until the next call. */
+const char* gdn_status_string(uint32_t bits);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

@@ -1,0 +1,37 @@
+"""Build the C-ABI library libgdn_mi355x.so (gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgdn_mi355x.so")
+SOURCES = ["gdn_api.cpp", "gdn_kernels.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         # packed fp32 ALU forms are kept out of every code object
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source into LIB (atomic replace).  Returns its path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and l.strip())
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, out))
+    if verbose and out:
+        print(out, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

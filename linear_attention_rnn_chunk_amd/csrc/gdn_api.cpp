@@ -1,0 +1,218 @@
+// gdn_api.cpp -- host side of the C ABI declared in include/gdn.h: argument
+// validation, supported-domain refusal, workspace sizing, status decoding.
+// Nothing here touches the device except through gdn::launch().
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+static inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+gdn_status make_plan(const gdn_problem* p, Plan* out) {
+  if (!p || !out) return GDN_E_NULL;
+  if (p->n_seq < 0 || p->total_tokens < 0 || p->seq_len < 0 || p->hk < 1 || p->hv < 1)
+    return GDN_E_SHAPE;
+  if (p->seq_len > 0 && (int64_t)p->n_seq * p->seq_len != p->total_tokens) return GDN_E_SHAPE;
+  if (p->hv % p->hk != 0) return GDN_E_UNSUPPORTED;
+  if (!(p->dk == 32 || p->dk == 64 || p->dk == 128)) return GDN_E_UNSUPPORTED;
+  if (!(p->dv == 32 || p->dv == 64 || p->dv == 128)) return GDN_E_UNSUPPORTED;
+  if (p->gate != GDN_GATE_HEAD && p->gate != GDN_GATE_KEY_CHANNEL) return GDN_E_UNSUPPORTED;
+  if (!(p->chunk == 0 || p->chunk == 32 || p->chunk == 64)) return GDN_E_UNSUPPORTED;
+  if (p->gate == GDN_GATE_KEY_CHANNEL && p->chunk == 64) return GDN_E_UNSUPPORTED;
+  if (p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_F32) return GDN_E_UNSUPPORTED;
+  if (p->o_dtype != GDN_BF16 && p->o_dtype != GDN_F32) return GDN_E_UNSUPPORTED;
+  if (p->arm != GDN_ARM_MFMA_BF16 && p->arm != GDN_ARM_FOLD_F32) return GDN_E_UNSUPPORTED;
+  if (p->compose != GDN_COMPOSE_AUTO && p->compose != GDN_COMPOSE_SPLIT &&
+      p->compose != GDN_COMPOSE_FUSED)
+    return GDN_E_UNSUPPORTED;
+  if (p->compose == GDN_COMPOSE_FUSED) return GDN_E_UNSUPPORTED;  // not built yet
+
+  Plan pl;
+  memset(&pl, 0, sizeof(pl));
+  pl.n_seq = p->n_seq;
+  pl.seq_len = p->seq_len;
+  pl.hk = p->hk;
+  pl.hv = p->hv;
+  pl.dk = p->dk;
+  pl.dv = p->dv;
+  pl.total = p->total_tokens;
+  pl.gate_channel = p->gate == GDN_GATE_KEY_CHANNEL;
+  pl.chunk = p->chunk ? p->chunk : (pl.gate_channel ? 32 : 64);
+  pl.arm_f32 = p->arm == GDN_ARM_FOLD_F32;
+  pl.qkv_f32 = p->qkv_dtype == GDN_F32;
+  pl.o_f32 = p->o_dtype == GDN_F32;
+  pl.fused = 0;
+  // The fixed-length form is chosen when seq_len > 0 or when there are no tokens at all;
+  // otherwise cu_seqlens must describe the sequences (checked in gdn_chunk_fwd).
+  pl.varlen = !(p->seq_len > 0 || p->total_tokens == 0);
+  const int64_t C = pl.chunk;
+  if (pl.varlen) {
+    if (p->total_tokens > INT32_MAX) return GDN_E_UNSUPPORTED;  // int32 cu_seqlens
+    pl.chunks_per_seq = 0;
+    pl.max_slots = (p->total_tokens + C - 1) / C + p->n_seq;
+  } else {
+    pl.chunks_per_seq = (int32_t)((p->seq_len + C - 1) / C);
+    pl.max_slots = (int64_t)p->n_seq * pl.chunks_per_seq;
+  }
+  // grid sizes are flattened into blockIdx.x
+  const int64_t heads_prep = pl.gate_channel ? pl.hv : pl.hk;
+  if (pl.max_slots * heads_prep > INT32_MAX) return GDN_E_UNSUPPORTED;
+  if ((int64_t)pl.n_seq * pl.hv * (pl.dv / 32) > INT32_MAX) return GDN_E_UNSUPPORTED;
+
+  const size_t esz = pl.arm_f32 ? 4 : 2;
+  size_t off = 0;
+  pl.off_table = off;
+  off = round_up(off + (pl.varlen ? 2 * sizeof(int32_t) * (size_t)(pl.n_seq + 1) : 0), 256);
+  const size_t tile = (size_t)pl.max_slots * pl.hv * C * C * esz;
+  pl.off_T = off;
+  off = round_up(off + tile, 256);
+  pl.off_P = off;
+  off = round_up(off + tile, 256);
+  pl.bytes = off;
+  *out = pl;
+  return GDN_OK;
+}
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_validate(const gdn_problem* p) {
+  gdn::Plan pl;
+  return gdn::make_plan(p, &pl);
+}
+
+gdn_status gdn_workspace_bytes(const gdn_problem* p, size_t* bytes) {
+  if (!bytes) return GDN_E_NULL;
+  gdn::Plan pl;
+  gdn_status s = gdn::make_plan(p, &pl);
+  if (s != GDN_OK) return s;
+  *bytes = pl.bytes;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* h0,
+                         const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  gdn::Plan pl;
+  gdn_status s = gdn::make_plan(p, &pl);
+  if (s != GDN_OK) return s;
+  if (!status) return GDN_E_NULL;
+  if (pl.total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_E_NULL;
+  if (p->seq_len > 0 && cu_seqlens) return GDN_E_SHAPE;  // one description of the sequences
+  if (pl.varlen && !cu_seqlens) return GDN_E_NULL;
+  if (pl.bytes > 0 && !workspace) return GDN_E_NULL;
+  if (workspace_bytes < pl.bytes) return GDN_E_WORKSPACE;
+  if (workspace && !gdn::aligned(workspace, 256)) return GDN_E_WORKSPACE;
+  if (!gdn::aligned(q, 16) || !gdn::aligned(k, 16) || !gdn::aligned(v, 16) || !gdn::aligned(o, 16) ||
+      !gdn::aligned(g, 4) || !gdn::aligned(beta, 4) || !gdn::aligned(h0, 4) ||
+      !gdn::aligned(hT, 4) || !gdn::aligned(status, 4) || !gdn::aligned(cu_seqlens, 4))
+    return GDN_E_UNSUPPORTED;
+
+  const size_t qsz = pl.qkv_f32 ? 4 : 2, osz = pl.o_f32 ? 4 : 2;
+  const size_t T = (size_t)pl.total;
+  const size_t nq = T * pl.hk * pl.dk * qsz, nv = T * pl.hv * pl.dv * qsz;
+  const size_t ng = T * pl.hv * (pl.gate_channel ? pl.dk : 1) * 4, nb = T * pl.hv * 4;
+  const size_t nh = (size_t)pl.n_seq * pl.hv * pl.dk * pl.dv * 4;
+  const size_t ncu = cu_seqlens ? (size_t)(pl.n_seq + 1) * 4 : 0;
+  const size_t no = T * pl.hv * pl.dv * osz;
+  struct R {
+    const void* p;
+    size_t n;
+  };
+  const R ins[] = {{q, nq}, {k, nq}, {v, nv}, {g, ng}, {beta, nb}, {h0, nh}, {cu_seqlens, ncu}};
+  const R outs[] = {{o, no}, {hT, nh}, {status, 4}, {workspace, pl.bytes}};
+  for (const R& a : outs) {
+    for (const R& b : ins)
+      if (gdn::overlap(a.p, a.n, b.p, b.n)) return GDN_E_ALIAS;
+    for (const R& b : outs)
+      if (&a != &b && gdn::overlap(a.p, a.n, b.p, b.n)) return GDN_E_ALIAS;
+  }
+  if (pl.n_seq == 0) return GDN_OK;  // nothing to compute
+
+  gdn::Params prm;
+  memset(&prm, 0, sizeof(prm));
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.g = g;
+  prm.beta = beta;
+  prm.h0 = h0;
+  prm.cu_seqlens = cu_seqlens;
+  prm.o = o;
+  prm.hT = hT;
+  prm.status = status;
+  char* ws = (char*)workspace;
+  prm.table = pl.varlen ? (int32_t*)(ws + pl.off_table) : nullptr;
+  prm.Tws = ws ? ws + pl.off_T : nullptr;
+  prm.Pws = ws ? ws + pl.off_P : nullptr;
+  prm.total = pl.total;
+  prm.n_seq = pl.n_seq;
+  prm.seq_len = pl.seq_len;
+  prm.hk = pl.hk;
+  prm.hv = pl.hv;
+  prm.dv = pl.dv;
+  prm.qkv_f32 = pl.qkv_f32;
+  prm.o_f32 = pl.o_f32;
+  prm.varlen = pl.varlen;
+  prm.chunks_per_seq = pl.chunks_per_seq;
+  prm.max_slots = pl.max_slots;
+  return gdn::launch(pl, prm, stream);
+}
+
+const char* gdn_error_string(int32_t code) {
+  switch (code) {
+    case GDN_OK: return "ok";
+    case GDN_E_NULL: return "a required pointer is NULL";
+    case GDN_E_SHAPE: return "sizes are negative or inconsistent";
+    case GDN_E_UNSUPPORTED: return "outside the supported domain (widths, chunk, dtype, alignment)";
+    case GDN_E_ALIAS: return "an output overlaps an input or another output";
+    case GDN_E_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case GDN_E_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown error code";
+  }
+}
+
+const char* gdn_status_string(uint32_t bits) {
+  static thread_local std::string s;
+  if (bits == 0) return "ok";
+  s.clear();
+  const struct {
+    uint32_t bit;
+    const char* name;
+  } names[] = {{GDN_ST_NONFINITE_INPUT, "nonfinite-input"},
+               {GDN_ST_GATE_DOMAIN, "gate-domain"},
+               {GDN_ST_BAD_SEQLENS, "bad-seqlens"},
+               {GDN_ST_NONFINITE_OUTPUT, "nonfinite-output"}};
+  uint32_t rest = bits;
+  for (auto& n : names) {
+    if (bits & n.bit) {
+      if (!s.empty()) s += "|";
+      s += n.name;
+      rest &= ~n.bit;
+    }
+  }
+  if (rest) {
+    char buf[32];
+    snprintf(buf, sizeof(buf), "%sunknown(0x%x)", s.empty() ? "" : "|", rest);
+    s += buf;
+  }
+  return s.c_str();
+}
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

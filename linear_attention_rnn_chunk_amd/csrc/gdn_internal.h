@@ -1,0 +1,50 @@
+// gdn_internal.h -- plan and kernel parameters shared by gdn_api.cpp and gdn_kernels.hip.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+// Everything a launch needs, resolved on the host from a gdn_problem.
+struct Plan {
+  int32_t n_seq, seq_len, hk, hv, dk, dv;
+  int64_t total;
+  int32_t gate_channel;  // 1: per-key-channel gate
+  int32_t chunk;         // 32 or 64
+  int32_t arm_f32;       // 1: fp32-fold arm
+  int32_t qkv_f32, o_f32;
+  int32_t fused;         // 1: fused composition
+  int32_t varlen;        // 1: cu_seqlens given
+  int32_t chunks_per_seq;  // fixed-length batches
+  int64_t max_slots;     // chunk slots the prep grid covers
+  // workspace carve-up (byte offsets)
+  size_t off_table, off_T, off_P, bytes;
+};
+
+// Kernel arguments (by value).
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* h0;
+  const int32_t* cu_seqlens;
+  void* o;
+  float* hT;
+  uint32_t* status;
+  int32_t* table;  // varlen: [n_seq+1] sanitised bounds, then [n_seq+1] chunk prefix
+  void* Tws;       // [slot][hv][C][C] solved T (arm element type)
+  void* Pws;       // [slot][hv][C][C] masked P (arm element type)
+  int64_t total;
+  int32_t n_seq, seq_len, hk, hv, dv;
+  int32_t qkv_f32, o_f32, varlen, chunks_per_seq;
+  int64_t max_slots;
+};
+
+gdn_status make_plan(const gdn_problem* p, Plan* plan);
+gdn_status launch(const Plan& plan, const Params& prm, void* stream);
+
+}  // namespace gdn

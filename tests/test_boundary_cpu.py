@@ -1,0 +1,149 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/gdn.h
+declares, and refuses unsupported or malformed calls on the host (nothing is
+launched on these paths, so fake device addresses are safe)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_rnn_chunk_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(gdn.LIBRARY_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    gdn.load()
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = set(re.findall(r"^\s*(?:gdn_status|const char\*|int32_t)\s+(gdn_\w+)\s*\(", hdr, re.M))
+    assert declared == set(gdn.EXPORTS)
+    lib = ctypes.CDLL(gdn.LIBRARY_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strings():
+    assert gdn.abi_version() == 1
+    assert gdn.error_string(0) == "ok"
+    for c in range(1, 7):
+        assert gdn.error_string(c) != "unknown error code"
+    assert gdn.error_string(99) == "unknown error code"
+    assert gdn.status_string(0) == "ok"
+    assert gdn.status_string(gdn.ST_NONFINITE_INPUT | gdn.ST_BAD_SEQLENS) == "nonfinite-input|bad-seqlens"
+    assert "unknown" in gdn.status_string(0x100)
+
+
+def P(**kw):
+    base = dict(n_seq=1, total_tokens=256, seq_len=256, hk=2, hv=6, dk=128, dv=128)
+    base.update(kw)
+    return gdn.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, gdn.GDN_OK),
+    (dict(dk=64, dv=32), gdn.GDN_OK),
+    (dict(gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_OK),
+    (dict(gate=gdn.GATE_KEY_CHANNEL, chunk=0), gdn.GDN_OK),
+    (dict(arm=gdn.ARM_FOLD_F32, qkv_dtype=gdn.F32, o_dtype=gdn.F32), gdn.GDN_OK),
+    (dict(n_seq=-1), gdn.GDN_E_SHAPE),
+    (dict(total_tokens=-5), gdn.GDN_E_SHAPE),
+    (dict(hk=0), gdn.GDN_E_SHAPE),
+    (dict(total_tokens=255), gdn.GDN_E_SHAPE),           # != n_seq * seq_len
+    (dict(hv=5), gdn.GDN_E_UNSUPPORTED),                 # hv % hk
+    (dict(dk=96), gdn.GDN_E_UNSUPPORTED),
+    (dict(dv=256), gdn.GDN_E_UNSUPPORTED),
+    (dict(chunk=16), gdn.GDN_E_UNSUPPORTED),
+    (dict(gate=gdn.GATE_KEY_CHANNEL, chunk=64), gdn.GDN_E_UNSUPPORTED),
+    (dict(gate=7), gdn.GDN_E_UNSUPPORTED),
+    (dict(qkv_dtype=3), gdn.GDN_E_UNSUPPORTED),
+    (dict(arm=2), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=9), gdn.GDN_E_UNSUPPORTED),
+])
+def test_validate_refusals(kw, code):
+    assert gdn.validate(P(**kw)) == code
+
+
+def test_validate_null_problem():
+    lib = gdn.load()
+    assert lib.gdn_validate(None) == gdn.GDN_E_NULL
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_workspace_bytes(ctypes.byref(P()), None) == gdn.GDN_E_NULL
+
+
+def test_workspace_bytes_scales_with_tiles():
+    # per chunk slot and value head: T and P, C x C each, bf16 (2 B) or fp32 (4 B)
+    b16 = gdn.workspace_bytes(P(chunk=64))
+    f32 = gdn.workspace_bytes(P(chunk=64, arm=gdn.ARM_FOLD_F32))
+    slots, hv, C = 4, 6, 64
+    assert b16 >= 2 * slots * hv * C * C * 2 and b16 < 2 * slots * hv * C * C * 2 + 1024
+    assert f32 >= 2 * slots * hv * C * C * 4
+    # packed form: slots bounded by ceil(total / C) + n_seq, plus the chunk table
+    pk = gdn.workspace_bytes(P(n_seq=3, seq_len=0, chunk=64))
+    assert pk >= 2 * (4 + 3) * hv * C * C * 2
+
+
+# fake, well-aligned device addresses: the host checks below return before any launch
+BASE = 1 << 40
+
+
+def _addrs(prob, qkv=2, osz=2):
+    T, hk, hv, dk, dv = prob.total_tokens, prob.hk, prob.hv, prob.dk, prob.dv
+    sizes = dict(q=T * hk * dk * qkv, k=T * hk * dk * qkv, v=T * hv * dv * qkv, g=T * hv * 4,
+                 beta=T * hv * 4, h0=prob.n_seq * hv * dk * dv * 4, o=T * hv * dv * osz,
+                 hT=prob.n_seq * hv * dk * dv * 4, status=4, ws=gdn.workspace_bytes(prob))
+    a, out = BASE, {}
+    for k_, n in sizes.items():
+        out[k_] = a
+        a += (n + 4095) // 4096 * 4096 + 4096
+    return out, sizes
+
+
+def _call(prob, a, ws_bytes=None, cu=None, **override):
+    lib = gdn.load()
+    args = dict(a)
+    args.update(override)
+    vp = ctypes.c_void_p
+    return lib.gdn_chunk_fwd(ctypes.byref(prob), vp(args["q"]), vp(args["k"]), vp(args["v"]),
+                             vp(args["g"]), vp(args["beta"]), vp(args["h0"]), vp(cu),
+                             vp(args["o"]), vp(args["hT"]), vp(args["status"]), vp(args["ws"]),
+                             ctypes.c_size_t(ws_bytes if ws_bytes is not None else
+                                             gdn.workspace_bytes(prob)), vp(0))
+
+
+def test_call_refusals_on_host():
+    prob = P()
+    a, s = _addrs(prob)
+    assert _call(prob, a, status=None) == gdn.GDN_E_NULL
+    assert _call(prob, a, q=None) == gdn.GDN_E_NULL
+    assert _call(prob, a, ws=None) == gdn.GDN_E_NULL
+    assert _call(prob, a, ws_bytes=gdn.workspace_bytes(prob) - 1) == gdn.GDN_E_WORKSPACE
+    assert _call(prob, a, ws=a["ws"] + 128) == gdn.GDN_E_WORKSPACE          # not 256-aligned
+    assert _call(prob, a, q=a["q"] + 8) == gdn.GDN_E_UNSUPPORTED            # not 16-aligned
+    assert _call(prob, a, hT=a["h0"]) == gdn.GDN_E_ALIAS                    # hT aliases h0
+    assert _call(prob, a, hT=a["h0"] + 4 * 128) == gdn.GDN_E_ALIAS          # partial overlap
+    assert _call(prob, a, o=a["v"]) == gdn.GDN_E_ALIAS
+    assert _call(prob, a, o=a["hT"]) == gdn.GDN_E_ALIAS
+    assert _call(prob, a, ws=a["o"]) == gdn.GDN_E_ALIAS
+    # fixed-length problem must not also carry cu_seqlens; packed problem needs them
+    assert _call(prob, a, cu=BASE - 4096) == gdn.GDN_E_SHAPE
+    pk = P(seq_len=0)
+    a2, _ = _addrs(pk)
+    assert _call(pk, a2) == gdn.GDN_E_NULL
+    # invalid problem is refused before pointers are looked at
+    assert _call(P(dk=48), a, ws_bytes=1 << 30) == gdn.GDN_E_UNSUPPORTED
+
+
+def test_empty_problem_returns_ok_without_device_work():
+    prob = P(n_seq=0, total_tokens=0, seq_len=0)
+    lib = gdn.load()
+    st = ctypes.c_void_p(BASE)
+    rc = lib.gdn_chunk_fwd(ctypes.byref(prob), None, None, None, None, None, None, None, None,
+                           None, st, None, ctypes.c_size_t(0), None)
+    assert rc == gdn.GDN_OK

@@ -1,0 +1,75 @@
+"""GPU parity: the HIP path against the fp64 token-serial oracle, element by element
+on the same seeded inputs, within the bounds recorded before the kernels were
+written (fp32-fold arm 1e-4, bf16-MFMA arm 2e-2, relative L2, NaN-aware)."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_rnn_chunk_amd import inputs
+from tests.gpu_util import BOUND, oracle_ref, rel, run_gpu, to_np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, arm, chunk=None, label=""):
+    o, hT, _ = run_gpu(inp, arm=arm, chunk=chunk)
+    o_ref, h_ref = oracle_ref(inp)
+    eo, eh = rel(to_np64(o), o_ref), rel(to_np64(hT), h_ref)
+    print("%s arm=%s chunk=%s rel-L2 o=%.3e hT=%.3e" % (label or inp.spec.name, arm, chunk, eo, eh),
+          flush=True)
+    assert eo <= BOUND[arm] and eh <= BOUND[arm], (eo, eh)
+    return eo, eh
+
+
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+def test_tiny_config(arm):
+    _check(inputs.make("tiny"), arm)
+
+
+GATE_MODES = {
+    "zero": dict(gate="head", gate_law="zero"),
+    "scalar": dict(gate="head", gate_law="clip5"),
+    "kda5": dict(gate="channel", gate_law="uniform5"),
+    "kda05": dict(gate="channel", gate_law="uniform05"),
+}
+
+
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", list(GATE_MODES))
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200, 4099])
+def test_length_and_gate_sweep(T, mode, arm):
+    kw = GATE_MODES[mode]
+    chunk = 32 if kw["gate"] == "channel" else 64
+    spec = inputs.Spec("sweep", (T,), 2, 4, 64, 64, qkv_dtype="bf16", h0=True, chunk=chunk,
+                       seed=100 + T, **kw)
+    _check(inputs.make(spec), arm, label="T=%d %s" % (T, mode))
+
+
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(32, 32), (32, 128), (64, 64), (128, 32), (128, 64), (128, 128)])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_widths_and_chunks(dk, dv, chunk, arm):
+    spec = inputs.Spec("widths", (150,), 1, 2, dk, dv, qkv_dtype="bf16", gate_law="clip5", h0=True,
+                       chunk=chunk, seed=dk * 7 + dv + chunk)
+    _check(inputs.make(spec), arm, chunk=chunk, label="dk=%d dv=%d" % (dk, dv))
+
+
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_packed_sequences_with_empty_and_short(arm, gate):
+    law = "uniform5" if gate == "channel" else "full"
+    spec = inputs.Spec("packed-small", (100, 0, 1, 64, 257, 31), 2, 6, 128, 128, qkv_dtype="bf16",
+                       gate=gate, gate_law=law, h0=True, chunk=32 if gate == "channel" else 64,
+                       packed=True, seed=55)
+    _check(inputs.make(spec), arm, label="packed %s" % gate)
+
+
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+def test_fp32_inputs_and_outputs(arm):
+    spec = inputs.Spec("f32io", (300,), 2, 2, 128, 128, qkv_dtype="f32", gate_law="half", h0=True,
+                       chunk=64, o_dtype="f32", seed=31)
+    _check(inputs.make(spec), arm)
+
+
+def test_single_sequence_config():
+    _check(inputs.make("single"), "bf16")
