@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunk-parallel gated delta-rule prefill on one MI355X.
+
+One step = one whole layer of the hot path (chunk tiles + serial scan + output)
+over the hybrid-model GDN layer: B=1, T=32768, 16 key heads / 48 value heads,
+dk = dv = 128, bf16 q/k/v, fp32 gate and beta, chunk 64, nonzero h0 (synthetic
+seeded inputs, resident in HBM before timing).  Prints one JSON line.
+
+Per-kernel durations come from HIP events recorded on the library's stream
+around each stage call inside the timed loop (the step is issued as a PREP call
+then a SCAN call on the same workspace, which is exactly the work of one full
+call).  The oracle (fp64 token-serial, OpenMP) is timed on a bounded sample of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+METRIC = "GDN chunk-prefill tokens/s per layer (HV=48,T=32k,d=128); MFMA % of peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(spec, chunk):
+    """Algorithmic bytes and flops of the two kernels for one layer.
+
+    prep (per chunk and key head, then per value head of the group):
+      bytes: q, k chunk rows + g, beta rows + T and P tiles written (bf16)
+      flops: K K^T and Q K^T lower halves 2 C^2 dk per key head; solve C^3/3 per value head
+    scan (per chunk and value head, 16 state columns per wave):
+      bytes: q, k rows (once per key head), v, o, g, beta, T and P tiles read; h0, hT
+      flops: K.H and Ktil^T R  4 C dk dv;  Q.H  2 C dk dv;  P.R and T.X at half  2 C^2 dv / 2 each
+    """
+    T, hk, hv, dk, dv = spec.tokens, spec.hk, spec.hv, spec.dk, spec.dv
+    n_seq = spec.n_seq
+    nch = sum((l + chunk - 1) // chunk for l in spec.seq_lens)
+    esz = 2
+    tile = chunk * chunk * esz
+    qk = 2 * T * hk * dk * 2
+    gb = 2 * T * hv * 4
+    prep_bytes = qk + gb + 2 * nch * hv * tile
+    prep_flops = nch * hk * 2 * chunk * chunk * dk + nch * hv * chunk ** 3 / 3
+    state = 2 * n_seq * hv * dk * dv * 4 if spec.h0 else n_seq * hv * dk * dv * 4
+    scan_bytes = qk + gb + 2 * T * hv * dv * 2 + 2 * nch * hv * tile + state
+    scan_flops = nch * hv * (6 * chunk * dk * dv + 2 * chunk * chunk * dv)
+    # compulsory bytes of the whole layer: q, k, v, g, beta in; o out; h0 in, hT out
+    layer_bytes = qk + gb + 2 * T * hv * dv * 2 + state
+    return dict(prep_bytes=prep_bytes, prep_flops=prep_flops, scan_bytes=scan_bytes,
+                scan_flops=scan_flops, chunks=nch, layer_bytes=layer_bytes)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("gdn_kernels.hip", "gdn_api.cpp", "gdn_internal.h"):
+        with open(os.path.join(ROOT, "linear_attention_rnn_chunk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, digest):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
+    taken on the current kernel sources (same digest); else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_digest:\s*(\w+)", txt)
+    if not m or m.group(1) != digest:
+        return None
+    m = re.search(r"^%s\s+bytes_per_launch:\s*([0-9.eE+]+)" % re.escape(kernel), txt, re.M)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(inp, budget_s):
+    """Oracle on the first N tokens of every value head (N calibrated to ~budget_s)."""
+    import numpy as np
+    import oracle
+
+    spec = inp.spec
+    q64, k64, v64 = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    g64, b64, h064 = inp.as_f64("g"), inp.as_f64("beta"), inp.as_f64("h0")
+    L0 = spec.seq_lens[0]
+
+    def run(ntok):
+        sl = slice(0, ntok)
+        t0 = time.perf_counter()
+        oracle.serial_fwd(q64[sl], k64[sl], v64[sl], g64[sl], b64[sl],
+                          None if h064 is None else h064[:1], seq_start=np.array([0, ntok]))
+        return time.perf_counter() - t0
+
+    cal = min(128, L0)
+    t_cal = run(cal)
+    ntok = int(min(L0, max(cal, cal * budget_s / max(t_cal, 1e-6))))
+    secs = run(ntok)
+    cores = min(oracle.max_threads(), spec.hv)
+    return dict(value=ntok / secs, unit="tokens/s", cores=cores, kind="oracle",
+                sample="fp64 token-serial oracle, all %d value heads of the hybrid layer over its "
+                       "first %d tokens (%.1f s)" % (spec.hv, ntok, secs))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="hybrid")
+    ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(see DESIGN.md for how the path would shard)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_rnn_chunk_amd import gdn, inputs
+
+    if not os.path.exists(gdn.LIBRARY_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    spec = inputs.CONFIGS[args.config]
+    chunk = args.chunk or spec.chunk
+    log("generating %s inputs (%d tokens)" % (spec.name, spec.tokens))
+    inp = inputs.make(spec)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def t(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    packed = spec.packed or len(set(spec.seq_lens)) > 1
+    if packed:
+        B, Tn = 1, spec.tokens
+        cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    else:
+        B, Tn = spec.n_seq, spec.seq_lens[0]
+        cu = None
+    shp = lambda a: a.reshape((B, Tn) + tuple(a.shape[1:]))
+    q, k, v, g, beta = (shp(t(getattr(inp, n))) for n in ("q", "k", "v", "g", "beta"))
+    h0 = t(inp.h0)
+    gate = gdn.GATE_KEY_CHANNEL if spec.gate == "channel" else gdn.GATE_HEAD
+    qdt = gdn.BF16 if spec.qkv_dtype == "bf16" else gdn.F32
+    odt_t = torch.bfloat16 if args.arm == "bf16" else torch.float32
+    arm = gdn.ARM_MFMA_BF16 if args.arm == "bf16" else gdn.ARM_FOLD_F32
+    mk = lambda stages: gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else Tn, spec.hk,
+                                         spec.hv, spec.dk, spec.dv, gate, chunk, qdt,
+                                         gdn.BF16 if odt_t == torch.bfloat16 else gdn.F32, arm,
+                                         gdn.COMPOSE_SPLIT, stages)
+    p_prep, p_scan = mk(gdn.STAGE_PREP), mk(gdn.STAGE_SCAN)
+    o = torch.empty((B, Tn, spec.hv, spec.dv), dtype=odt_t, device=dev)
+    hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(gdn.workspace_bytes(p_prep), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = gdn.chunk_fwd_raw(p_prep, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= gdn.chunk_fwd_raw(p_scan, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
+        if ev is not None:
+            ev[2].record(stream)
+        if rc:
+            raise gdn.GdnError(rc, "gdn_chunk_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(status.item()):
+        raise gdn.GdnStatusError(int(status.item()))
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    if int(status.item()):
+        raise gdn.GdnStatusError(int(status.item()))
+    log("ms/step %.4f (prep %.4f, scan %.4f), wall %.3f s for %d steps"
+        % (ms_step, prep_ms, scan_ms, wall, args.steps))
+
+    alg = algorithmic(spec, chunk)
+    peak_mfma = MFMA_BF16_PEAK_TFLOPS if args.arm == "bf16" else MFMA_F32_PEAK_TFLOPS
+    dom = "scan" if scan_ms >= prep_ms else "prep"
+    dom_ms = scan_ms if dom == "scan" else prep_ms
+    dom_bytes = alg[dom + "_bytes"]
+    achieved_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    kernel_name = "gdn_scan" if dom == "scan" else "gdn_prep"
+    digest = source_digest()
+    traffic = traffic_from_profiles(kernel_name, digest)
+    tokens_s = spec.tokens / (ms_step * 1e-3)
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if args.arm == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s GDN layer prefill: B=%d, T=%d, %d key / %d value heads, "
+                               "dk=dv=%d, %s gate, chunk %d%s"
+                               % (spec.name, spec.n_seq, spec.tokens // spec.n_seq, spec.hk, spec.hv,
+                                  spec.dk, "per-head" if gate == gdn.GATE_HEAD else "per-key-channel",
+                                  chunk, ", h0" if spec.h0 else ""),
+                   "tokens": spec.tokens, "arm": args.arm, "composition": "split"},
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel_ms": dom_ms, "algorithmic_bytes": dom_bytes},
+        "mfma": {"definition": "algorithmic flops / kernel time / dense peak",
+                 "peak_tflops": peak_mfma,
+                 "prep_frac": alg["prep_flops"] / (prep_ms * 1e-3) / (peak_mfma * 1e12),
+                 "scan_frac": alg["scan_flops"] / (scan_ms * 1e-3) / (peak_mfma * 1e12),
+                 "layer_frac": (alg["prep_flops"] + alg["scan_flops"]) / (ms_step * 1e-3)
+                 / (peak_mfma * 1e12)},
+        "kernels_ms": {"prep": prep_ms, "scan": scan_ms},
+        "layer_hbm_frac": alg["layer_bytes"] / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "source_digest": digest,
+    }
+    if not args.no_cpu:
+        log("timing the oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,6 +66,12 @@ enum { GDN_ARM_MFMA_BF16 = 0, GDN_ARM_FOLD_F32 = 1 };
  * (one kernel computes the chunk tiles and runs the scan).  AUTO picks the
  * measured default for the problem. */
 enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2 };
+/* Stages of the split composition a call runs.  0 (or PREP|SCAN) runs both.  A
+ * SCAN-only call consumes the chunk tiles a previous PREP call (same problem, same
+ * inputs, same workspace) left in the workspace; the caller orders the two calls,
+ * e.g. on one stream.  This lets the sequence-parallel tile stage of a layer run
+ * ahead of its scan, and lets each stage be timed on its own. */
+enum { GDN_STAGE_ALL = 0, GDN_STAGE_PREP = 1, GDN_STAGE_SCAN = 2 };
 
 typedef struct gdn_problem {
   int32_t n_seq;        /* number of sequences, >= 0 */
@@ -82,6 +88,7 @@ typedef struct gdn_problem {
   int32_t o_dtype;      /* GDN_BF16 or GDN_F32 for o */
   int32_t arm;          /* GDN_ARM_MFMA_BF16 or GDN_ARM_FOLD_F32 */
   int32_t compose;      /* GDN_COMPOSE_* */
+  int32_t stages;       /* GDN_STAGE_ALL, or PREP / SCAN alone (split composition) */
 } gdn_problem;
 
 /* Checks a problem description on the host (no device work).  Returns GDN_OK,

@@ -30,6 +30,7 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
       p->compose != GDN_COMPOSE_FUSED)
     return GDN_E_UNSUPPORTED;
   if (p->compose == GDN_COMPOSE_FUSED) return GDN_E_UNSUPPORTED;  // not built yet
+  if (p->stages < 0 || p->stages > (GDN_STAGE_PREP | GDN_STAGE_SCAN)) return GDN_E_UNSUPPORTED;
 
   Plan pl;
   memset(&pl, 0, sizeof(pl));
@@ -46,6 +47,8 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   pl.qkv_f32 = p->qkv_dtype == GDN_F32;
   pl.o_f32 = p->o_dtype == GDN_F32;
   pl.fused = 0;
+  pl.run_prep = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_PREP);
+  pl.run_scan = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_SCAN);
   // The fixed-length form is chosen when seq_len > 0 or when there are no tokens at all;
   // otherwise cu_seqlens must describe the sequences (checked in gdn_chunk_fwd).
   pl.varlen = !(p->seq_len > 0 || p->total_tokens == 0);
@@ -72,6 +75,14 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   off = round_up(off + tile, 256);
   pl.off_P = off;
   off = round_up(off + tile, 256);
+  // per-channel gate: gated operands and chunk decay, produced by the sequence-parallel
+  // stage so the scan streams them instead of re-deriving them serially
+  const size_t gated = pl.gate_channel ? (size_t)pl.max_slots * pl.hv * 3 * C * pl.dk * esz : 0;
+  const size_t decb = pl.gate_channel ? (size_t)pl.max_slots * pl.hv * pl.dk * 4 : 0;
+  pl.off_G = off;
+  off = round_up(off + gated, 256);
+  pl.off_D = off;
+  off = round_up(off + decb, 256);
   pl.bytes = off;
   *out = pl;
   return GDN_OK;
@@ -159,6 +170,8 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   prm.table = pl.varlen ? (int32_t*)(ws + pl.off_table) : nullptr;
   prm.Tws = ws ? ws + pl.off_T : nullptr;
   prm.Pws = ws ? ws + pl.off_P : nullptr;
+  prm.Gws = (ws && pl.gate_channel) ? ws + pl.off_G : nullptr;
+  prm.Dws = (ws && pl.gate_channel) ? (float*)(ws + pl.off_D) : nullptr;
   prm.total = pl.total;
   prm.n_seq = pl.n_seq;
   prm.seq_len = pl.seq_len;

@@ -16,11 +16,12 @@ struct Plan {
   int32_t arm_f32;       // 1: fp32-fold arm
   int32_t qkv_f32, o_f32;
   int32_t fused;         // 1: fused composition
+  int32_t run_prep, run_scan;  // stages to launch
   int32_t varlen;        // 1: cu_seqlens given
   int32_t chunks_per_seq;  // fixed-length batches
   int64_t max_slots;     // chunk slots the prep grid covers
   // workspace carve-up (byte offsets)
-  size_t off_table, off_T, off_P, bytes;
+  size_t off_table, off_T, off_P, off_G, off_D, bytes;
 };
 
 // Kernel arguments (by value).
@@ -38,6 +39,8 @@ struct Params {
   int32_t* table;  // varlen: [n_seq+1] sanitised bounds, then [n_seq+1] chunk prefix
   void* Tws;       // [slot][hv][C][C] solved T (arm element type)
   void* Pws;       // [slot][hv][C][C] masked P (arm element type)
+  void* Gws;       // per-channel gate: [slot][hv][3][C][dk] e^{G} K, e^{G_C-G} K, e^{G} Q
+  float* Dws;      // per-channel gate: [slot][hv][dk] e^{G_C}
   int64_t total;
   int32_t n_seq, seq_len, hk, hv, dv;
   int32_t qkv_f32, o_f32, varlen, chunks_per_seq;

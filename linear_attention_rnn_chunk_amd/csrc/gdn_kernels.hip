@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -41,6 +43,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // native vector (registers, not a struct)
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 extern __shared__ __align__(16) unsigned char gdn_smem[];
@@ -405,16 +408,69 @@ __device__ void solve_unit_lower(const float* Am, float* Tm, int tid) {
   }
 }
 
+// ------------------------------------------------ 16-byte staging -------
+__device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
+  return *(const u32x4*)((const char*)base + byte_off);
+}
+
+template <bool QF32>
+__device__ __forceinline__ bool nonfinite16(u32x4 a) {
+  if constexpr (QF32) {
+    return f_nonfinite(__uint_as_float(a.x)) || f_nonfinite(__uint_as_float(a.y)) ||
+           f_nonfinite(__uint_as_float(a.z)) || f_nonfinite(__uint_as_float(a.w));
+  } else {
+    return bf_nonfinite(a.x) || bf_nonfinite(a.y) || bf_nonfinite(a.z) || bf_nonfinite(a.w);
+  }
+}
+
+// 16 input bytes (8 bf16 or 4 fp32) -> the same elements in the arm's LDS type
+template <class Arm, bool QF32>
+__device__ __forceinline__ void put16(u32x4 a, typename Arm::T* dst) {
+  if constexpr (sizeof(typename Arm::T) == 2) {
+    if constexpr (QF32) {
+      const uint32_t w0 = (uint32_t)f2bf(__uint_as_float(a.x)) | ((uint32_t)f2bf(__uint_as_float(a.y)) << 16);
+      const uint32_t w1 = (uint32_t)f2bf(__uint_as_float(a.z)) | ((uint32_t)f2bf(__uint_as_float(a.w)) << 16);
+      *(uint2*)dst = (uint2){w0, w1};
+    } else {
+      *(u32x4*)dst = a;
+    }
+  } else {
+    if constexpr (QF32) {
+      *(u32x4*)dst = a;
+    } else {
+      float4* d = (float4*)dst;
+      d[0] = (float4){__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
+                      __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
+      d[1] = (float4){__uint_as_float(a.z << 16), __uint_as_float(a.z & 0xFFFF0000u),
+                      __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xFFFF0000u)};
+    }
+  }
+}
+
+// 16 input bytes -> fp32 in LDS
+template <bool QF32>
+__device__ __forceinline__ void put16f(u32x4 a, float* dst) {
+  if constexpr (QF32) {
+    *(u32x4*)dst = a;
+  } else {
+    float4* d = (float4*)dst;
+    d[0] = (float4){__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
+                    __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
+    d[1] = (float4){__uint_as_float(a.z << 16), __uint_as_float(a.z & 0xFFFF0000u),
+                    __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xFFFF0000u)};
+  }
+}
+
 // ----------------------------------------------------------- prep -------
 template <class Arm, int DK, int C>
 constexpr size_t prep_lds_bytes(bool kda) {
-  return (size_t)(kda ? 3 : 2) * C * (DK + Arm::PAD) * sizeof(typename Arm::T)  // operands
+  return (size_t)(kda ? 6 : 2) * C * (DK + Arm::PAD) * sizeof(typename Arm::T)  // operands
          + 2 * (size_t)C * (C + 4) * sizeof(float)                             // A, T (fp32)
          + (size_t)C * C * sizeof(typename Arm::T)                             // P staging
          + 2 * (size_t)C * sizeof(float);                                      // G, beta
 }
 
-template <class Arm, int DK, int C, bool KDA>
+template <class Arm, int DK, int C, bool KDA, bool QF32>
 __global__ __launch_bounds__(256) void gdn_prep(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
@@ -433,7 +489,8 @@ __global__ __launch_bounds__(256) void gdn_prep(Params p) {
   T* X0 = (T*)gdn_smem;  // K (scalar gate) or K*e^{G-Gm} (per-channel gate)
   T* X1 = X0 + C * KP;   // Q                or K*e^{Gm-G}
   T* X2 = X1 + C * KP;   // --               or Q*e^{G-Gm}
-  float* Am = (float*)(X0 + (KDA ? 3 : 2) * C * KP);
+  T* Y0 = X2 + C * KP;   // per-channel gate, for the scan: e^{G} K, e^{G_C-G} K, e^{G} Q
+  float* Am = (float*)(X0 + (KDA ? 6 : 2) * C * KP);
   float* Tm = Am + C * AP;
   T* Pst = (T*)(Tm + C * AP);
   float* Gs = (float*)(Pst + C * C);
@@ -441,19 +498,27 @@ __global__ __launch_bounds__(256) void gdn_prep(Params p) {
   uint32_t bad = 0;
 
   if constexpr (!KDA) {
-    for (int idx = tid; idx < C * DK / 8; idx += 256) {
-      const int r = idx / (DK / 8), c8 = idx % (DK / 8);
-      T* dk_ = X0 + r * KP + 8 * c8;
-      T* dq_ = X1 + r * KP + 8 * c8;
-      if (r < L) {
-        const int64_t e = ((t0 + r) * p.hk + kh) * (int64_t)DK + 8 * c8;
-        const bool bk = load8<Arm>(p.k, e, p.qkv_f32, dk_);
-        const bool bq = load8<Arm>(p.q, e, p.qkv_f32, dq_);
-        if (bk || bq) bad |= GDN_ST_NONFINITE_INPUT;
-      } else {
-        zero8<Arm>(dk_);
-        zero8<Arm>(dq_);
-      }
+    // every load first (rows past the chunk end re-read the last valid row, in bounds),
+    // then the stores; no branch around a load
+    constexpr int EPC = QF32 ? 4 : 8, ESZ = QF32 ? 4 : 2, NP = C * DK / EPC;
+    constexpr int NL = (NP + 255) / 256;
+    u32x4 ka[NL], qa[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int idx = tid + 256 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
+      const int rr = (r < L ? r : L - 1) % C;  // pieces past NP (tiny widths) re-read row 0..C-1
+      const int64_t off = (((t0 + rr) * p.hk + kh) * (int64_t)DK + c * EPC) * ESZ;
+      ka[j] = ld16(p.k, off);
+      qa[j] = ld16(p.q, off);
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int idx = tid + 256 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
+      if (NP % 256 != 0 && idx >= NP) break;
+      const u32x4 kz = (r < L) ? ka[j] : (u32x4)(0u), qz = (r < L) ? qa[j] : (u32x4)(0u);
+      if (nonfinite16<QF32>(kz) || nonfinite16<QF32>(qz)) bad |= GDN_ST_NONFINITE_INPUT;
+      put16<Arm, QF32>(kz, X0 + r * KP + c * EPC);
+      put16<Arm, QF32>(qz, X1 + r * KP + c * EPC);
     }
   } else {
     // per-channel gate: one thread per key channel walks the chunk rows; factors are
@@ -466,33 +531,46 @@ __global__ __launch_bounds__(256) void gdn_prep(Params p) {
       float acc = 0.f;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        float x = 0.f;
-        if (r < L) {
-          x = p.g[((t0 + r) * p.hv + hv) * (int64_t)DK + d];
-          if (f_nonfinite(x)) bad |= GDN_ST_NONFINITE_INPUT;
-          else if (x > 0.f || x < -5.f) bad |= GDN_ST_GATE_DOMAIN;
-        }
+        const int rr = r < L ? r : L - 1;
+        const float xl = p.g[((t0 + rr) * p.hv + hv) * (int64_t)DK + d];
+        const float x = r < L ? xl : 0.f;
+        if (f_nonfinite(x)) bad |= GDN_ST_NONFINITE_INPUT;
+        else if (x > 0.f || x < -5.f) bad |= GDN_ST_GATE_DOMAIN;
         acc += x;
         G[r] = acc;
       }
       const float Gm = G[C / 2];
+      const float GC = G[C - 1];
+      T* Y1 = Y0 + C * KP;
+      T* Y2 = Y1 + C * KP;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        float kf = 0.f, qf = 0.f;
-        if (r < L) {
-          const int64_t e = ((t0 + r) * p.hk + kh) * (int64_t)DK + d;
-          kf = load1(p.k, e, p.qkv_f32);
-          qf = load1(p.q, e, p.qkv_f32);
-          if (f_nonfinite(kf) || f_nonfinite(qf)) bad |= GDN_ST_NONFINITE_INPUT;
-        }
+        const int rr = r < L ? r : L - 1;
+        const int64_t e = ((t0 + rr) * p.hk + kh) * (int64_t)DK + d;
+        const float kl = load1(p.k, e, QF32), ql = load1(p.q, e, QF32);
+        const float kf = r < L ? kl : 0.f, qf = r < L ? ql : 0.f;
+        if (f_nonfinite(kf) || f_nonfinite(qf)) bad |= GDN_ST_NONFINITE_INPUT;
         const float up = nexp(fminf(G[r] - Gm, 85.f)), dn = nexp(fminf(Gm - G[r], 85.f));
         X0[r * KP + d] = Arm::cvt(kf * up);
         X1[r * KP + d] = Arm::cvt(kf * dn);
         X2[r * KP + d] = Arm::cvt(qf * up);
+        const float eg = nexp(G[r]);
+        Y0[r * KP + d] = Arm::cvt(eg * kf);
+        Y1[r * KP + d] = Arm::cvt(nexp(GC - G[r]) * kf);
+        Y2[r * KP + d] = Arm::cvt(eg * qf);
       }
+      p.Dws[(slot * p.hv + hv) * (int64_t)DK + d] = nexp(GC);
     }
   }
   __syncthreads();
+  if constexpr (KDA) {
+    constexpr int EPT = 16 / (int)sizeof(T);
+    T* Gg = (T*)p.Gws + (slot * p.hv + head) * (int64_t)(3 * C * DK);
+    for (int idx = tid; idx < 3 * C * DK / EPT; idx += 256) {
+      const int e0 = idx * EPT, m = e0 / (C * DK), r = (e0 / DK) % C, c = e0 % DK;
+      *(uint4*)(Gg + e0) = *(const uint4*)(Y0 + (m * C + r) * KP + c);
+    }
+  }
 
   // Products on MFMA: tile list = lower tiles (rt >= st) of the two C x C products.
   // scalar gate: KK^T and QK^T;  per-channel gate: Kup Kdn^T and Qup Kdn^T.
@@ -580,9 +658,18 @@ __global__ __launch_bounds__(256) void gdn_prep(Params p) {
     for (int idx = tid; idx < C * C / 8; idx += 256) copy8<Arm>(Pst + 8 * idx, Pg + 8 * idx);
     solve_unit_lower<C>(Am, Tm, tid);
     T* Tg = (T*)p.Tws + (slot * p.hv + hv) * (int64_t)(C * C);
-    for (int idx = tid; idx < C * C; idx += 256) {
-      const int r = idx / C, s = idx % C;
-      Tg[idx] = Arm::cvt(Tm[r * AP + s]);
+    constexpr int EPT = 16 / (int)sizeof(T);
+    for (int idx = tid; idx < C * C / EPT; idx += 256) {
+      const int e0 = idx * EPT, r = e0 / C, c = e0 % C;
+      const float* src = Tm + r * AP + c;
+      if constexpr (sizeof(T) == 2) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f2bf(src[2 * j]) | ((uint32_t)f2bf(src[2 * j + 1]) << 16);
+        *(u32x4*)(Tg + e0) = w;
+      } else {
+        *(float4*)(Tg + e0) = *(const float4*)src;
+      }
     }
     __syncthreads();
   }
@@ -590,21 +677,56 @@ __global__ __launch_bounds__(256) void gdn_prep(Params p) {
 }
 
 // ----------------------------------------------------------- scan -------
+// Sizes of the loaders' staging in 16-byte pieces per loader thread (128 of them).
+template <class Arm, int DK, int C, bool KDA, bool QF32>
+struct ScanStageDims {
+  using T = typename Arm::T;
+  static constexpr int EPC = QF32 ? 4 : 8;                           // input elements per 16 bytes
+  static constexpr int NKQ = C * DK / EPC / 128;                     // K (and Q) rows
+  static constexpr int NTP = C * C * (int)sizeof(T) / 16 / 128;      // T (and P)
+  static constexpr int NV = C * 32 / EPC / 128;                      // the 32 V columns
+  static constexpr int NG = 3 * C * DK * (int)sizeof(T) / 16 / 128;  // gated operands
+};
+
+// LDS of one chunk buffer of the scan: operands, T, P, V (fp32), row scalars.
 template <class Arm, int DK, int C>
-constexpr size_t scan_lds_bytes(bool kda) {
+constexpr size_t scan_buf_bytes(bool kda) {
   return (size_t)(kda ? 3 : 2) * C * (DK + Arm::PAD) * sizeof(typename Arm::T)  // K [, K~], Q
          + 2 * (size_t)C * (C + Arm::PAD) * sizeof(typename Arm::T)            // T, P
          + (size_t)C * 36 * sizeof(float)                                      // V (32 columns)
          + (4 * (size_t)C + DK + 4) * sizeof(float);                           // row scalars
 }
+// Two chunk buffers (the next chunk is written while the current one is read) when they
+// fit in the 160 KiB of LDS, else one.
+template <class Arm, int DK, int C>
+constexpr int scan_nbuf(bool kda) { return 2 * scan_buf_bytes<Arm, DK, C>(kda) <= 150 * 1024 ? 2 : 1; }
+template <class Arm, int DK, int C>
+constexpr size_t scan_lds_bytes(bool kda) {
+  return scan_nbuf<Arm, DK, C>(kda) * ((scan_buf_bytes<Arm, DK, C>(kda) + 255) / 256 * 256);
+}
 
-template <class Arm, int DK, int C, bool KDA>
-__global__ __launch_bounds__(128) void gdn_scan(Params p) {
+// Scan workgroup: 4 waves for 32 state columns of one (sequence, value head).
+//   waves 0, 1  compute: each owns 16 state columns; its fp32 state stays in MFMA
+//               accumulators and only its matrix products run on its SIMD
+//   waves 2, 3  loaders: bring chunk operands from global memory through registers into
+//               the LDS chunk buffers, two chunks ahead (two register sets), and run the
+//               in-chunk gate sweep
+// One barrier per chunk hands a filled buffer from the loaders to the compute waves.
+template <class Arm, int DK, int C, bool KDA, bool QF32>
+__global__ __launch_bounds__(256) void gdn_scan(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
+  using Stage = ScanStageDims<Arm, DK, C, KDA, QF32>;
   constexpr int NT = C / 16, NBC = C / 32, NTK = DK / 16, NBK = DK / 32;
   constexpr int KP = DK + Arm::PAD, CP = C + Arm::PAD, VP = 36;
-  const int tid = threadIdx.x, lane = tid & 63, u = tid >> 6, i = lane & 15, g = lane >> 4;
+  constexpr int EPC = Stage::EPC, ESZ = QF32 ? 4 : 2;
+  constexpr int EPT = 16 / (int)sizeof(T);  // arm elements per 16 bytes
+  constexpr int NBUF = scan_nbuf<Arm, DK, C>(KDA);
+  constexpr size_t BUF = (scan_buf_bytes<Arm, DK, C>(KDA) + 255) / 256 * 256;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
+  const bool loader = wave >= 2;
+  const int u = wave & 1;            // compute: state unit; loader: loader index
+  const int ltid = tid & 127;        // loader thread index 0..127
   const int DV = p.dv, nslice = DV / 32;
   int bid = blockIdx.x;
   const int slice = bid % nslice;
@@ -612,19 +734,27 @@ __global__ __launch_bounds__(128) void gdn_scan(Params p) {
   const int h = bid % p.hv;
   const int n = bid / p.hv;
   const int kh = h / (p.hv / p.hk);
-  const int col0 = 32 * slice + 16 * u;  // first value column of this wave
+  const int col0 = 32 * slice + 16 * u;  // compute waves: first value column
 
-  T* Ks = (T*)gdn_smem;                   // K (scalar gate) or beta e^{G} K (per channel)
-  T* Kl = KDA ? Ks + C * KP : Ks;         // per channel: e^{G_C - G} K
-  T* Qs = Ks + (KDA ? 2 : 1) * C * KP;    // Q or e^{G} Q
-  T* Ts = Qs + C * KP;
-  T* Ps = Ts + C * CP;
-  float* Vs = (float*)(Ps + C * CP);
-  float* sb_ = Vs + C * VP;  // beta
-  float* sbe = sb_ + C;      // beta e^{G}
-  float* seg = sbe + C;      // e^{G}
-  float* sel = seg + C;      // e^{G_C - G}
-  float* sdec = sel + C;     // e^{G_C} per key channel (per-channel gate) / [0] scalar
+  struct Buf {
+    T *Ks, *Kl, *Qs, *Ts, *Ps;
+    float *Vs, *sb_, *sbe, *seg, *sel, *sdec;
+  };
+  auto buf_at = [&](int b) __attribute__((always_inline)) {
+    Buf B;
+    B.Ks = (T*)(gdn_smem + b * BUF);      // K (per-head gate) or e^{G} K (per channel)
+    B.Kl = KDA ? B.Ks + C * KP : B.Ks;    // per channel: e^{G_C - G} K
+    B.Qs = B.Ks + (KDA ? 2 : 1) * C * KP; // Q or e^{G} Q
+    B.Ts = B.Qs + C * KP;
+    B.Ps = B.Ts + C * CP;
+    B.Vs = (float*)(B.Ps + C * CP);
+    B.sb_ = B.Vs + C * VP;  // beta
+    B.sbe = B.sb_ + C;      // beta e^{G}
+    B.seg = B.sbe + C;      // e^{G}
+    B.sel = B.seg + C;      // e^{G_C - G}
+    B.sdec = B.sel + C;     // e^{G_C} per key channel (per-channel gate) / [0] per-head gate
+    return B;
+  };
 
   int64_t s0, s1, slot0;
   if (p.varlen) {
@@ -636,153 +766,212 @@ __global__ __launch_bounds__(128) void gdn_scan(Params p) {
     s1 = s0 + p.seq_len;
     slot0 = (int64_t)n * p.chunks_per_seq;
   }
+  const int64_t nch = (s1 - s0 + C - 1) / C;
   uint32_t bad = 0;
 
-  f32x4 H[NTK];
-  const int64_t hbase = ((int64_t)n * p.hv + h) * DK * (int64_t)DV;
-#pragma unroll
-  for (int t = 0; t < NTK; ++t) {
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int d = 16 * t + 4 * g + ii;
-      float x = 0.f;
-      if (p.h0) {
-        x = p.h0[hbase + (int64_t)d * DV + col0 + i];
-        if (f_nonfinite(x)) bad |= GDN_ST_NONFINITE_INPUT;
-      }
-      H[t][ii] = x;
-    }
-  }
+  // Loader staging: two register sets (chunks in flight).  Per-head gate: raw K and Q
+  // rows, gate and beta of row `lane` (first loader wave).  Per-channel gate: the gated
+  // operands from the sequence-parallel stage, beta, e^{G_C[d]}.
+  constexpr int NK = KDA ? 1 : Stage::NKQ, NG = KDA ? Stage::NG : 1;
+  u32x4 sk[2][NK], sq[2][NK], skg[2][NG], stt[2][Stage::NTP], spp[2][Stage::NTP], sv[2][Stage::NV];
+  float sg[2] = {0.f, 0.f}, sbt[2] = {0.f, 0.f}, sdc[2] = {0.f, 0.f};
 
-  const int64_t nch = (s1 - s0 + C - 1) / C;
-  for (int64_t ci = 0; ci < nch; ++ci) {
+  // ---- loaders: global -> register set `rs` for chunk ci (branch-free: rows past the
+  //      chunk end re-read its last row, in bounds, and are zeroed by a select)
+  auto issue = [&](int rs, int64_t ci) __attribute__((always_inline)) {
     const int64_t t0 = s0 + ci * C;
     const int L = (int)min64(C, s1 - t0);
     const int64_t slot = slot0 + ci;
-    // ---- fill: gate scalars, operands, T, P, V
     if constexpr (!KDA) {
-      if (u == 0) {
-        const int r = lane;
-        float x = 0.f, b = 0.f;
-        if (r < L) {
-          const int64_t e = (t0 + r) * p.hv + h;
-          x = p.g[e];
-          b = p.beta[e];
-        }
-        const float G = wave_prefix_sum(x, lane);
-        const float GC = __shfl(G, C - 1, 64);
-        if (r < C) {
-          const float eg = nexp(G);
-          sb_[r] = b;
-          sbe[r] = b * eg;
-          seg[r] = eg;
-          sel[r] = nexp(GC - G);
-        }
-        if (r == 0) sdec[0] = nexp(GC);
+#pragma unroll
+      for (int j = 0; j < Stage::NKQ; ++j) {
+        const int idx = ltid + 128 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
+        const int rr = r < L ? r : L - 1;
+        const int64_t off = (((t0 + rr) * p.hk + kh) * (int64_t)DK + c * EPC) * ESZ;
+        const u32x4 a = ld16(p.k, off), b = ld16(p.q, off);
+        sk[rs][j] = (r < L) ? a : (u32x4)(0u);
+        sq[rs][j] = (r < L) ? b : (u32x4)(0u);
       }
-      for (int idx = tid; idx < C * DK / 8; idx += 128) {
-        const int r = idx / (DK / 8), c8 = idx % (DK / 8);
-        T* dk_ = Ks + r * KP + 8 * c8;
-        T* dq_ = Qs + r * KP + 8 * c8;
-        if (r < L) {
-          const int64_t e = ((t0 + r) * p.hk + kh) * (int64_t)DK + 8 * c8;
-          load8<Arm>(p.k, e, p.qkv_f32, dk_);
-          load8<Arm>(p.q, e, p.qkv_f32, dq_);
-        } else {
-          zero8<Arm>(dk_);
-          zero8<Arm>(dq_);
-        }
+      if (u == 0) {
+        const int rr = lane < L ? lane : L - 1;
+        const float x = p.g[(t0 + rr) * p.hv + h], b = p.beta[(t0 + rr) * p.hv + h];
+        sg[rs] = (lane < L) ? x : 0.f;
+        sbt[rs] = (lane < L) ? b : 0.f;
       }
     } else {
       if (u == 0) {
-        const int r = lane;
-        if (r < C) sb_[r] = (r < L) ? p.beta[(t0 + r) * p.hv + h] : 0.f;
+        const float b = p.beta[(t0 + (lane < L ? lane : L - 1)) * p.hv + h];
+        sbt[rs] = (lane < L) ? b : 0.f;
       }
-      if (tid < DK) {
-        const int d = tid;
-        float G[C];
-        float acc = 0.f;
+      const u32x4* Gg = (const u32x4*)((const T*)p.Gws + (slot * p.hv + h) * (int64_t)(3 * C * DK));
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-          acc += (r < L) ? p.g[((t0 + r) * p.hv + h) * (int64_t)DK + d] : 0.f;
-          G[r] = acc;
-        }
-        const float GC = acc;
-        sdec[d] = nexp(GC);
+      for (int j = 0; j < Stage::NG; ++j) skg[rs][j] = Gg[ltid + 128 * j];
+      if (ltid < DK) sdc[rs] = p.Dws[(slot * p.hv + h) * (int64_t)DK + ltid];
+    }
+    const u32x4* Tg = (const u32x4*)((const T*)p.Tws + (slot * p.hv + h) * (int64_t)(C * C));
+    const u32x4* Pg = (const u32x4*)((const T*)p.Pws + (slot * p.hv + h) * (int64_t)(C * C));
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-          float kf = 0.f, qf = 0.f, b = 0.f;
-          if (r < L) {
-            const int64_t e = ((t0 + r) * p.hk + kh) * (int64_t)DK + d;
-            kf = load1(p.k, e, p.qkv_f32);
-            qf = load1(p.q, e, p.qkv_f32);
-            b = p.beta[(t0 + r) * p.hv + h];
-          }
-          const float eg = nexp(G[r]);
-          Ks[r * KP + d] = Arm::cvt(b * eg * kf);
-          Kl[r * KP + d] = Arm::cvt(nexp(GC - G[r]) * kf);
-          Qs[r * KP + d] = Arm::cvt(eg * qf);
-        }
-      }
+    for (int j = 0; j < Stage::NTP; ++j) {
+      stt[rs][j] = Tg[ltid + 128 * j];
+      spp[rs][j] = Pg[ltid + 128 * j];
     }
-    {
-      const T* Tg = (const T*)p.Tws + (slot * p.hv + h) * (int64_t)(C * C);
-      const T* Pg = (const T*)p.Pws + (slot * p.hv + h) * (int64_t)(C * C);
-      for (int idx = tid; idx < C * C / 8; idx += 128) {
-        const int r = idx / (C / 8), c8 = idx % (C / 8);
-        copy8<Arm>(Tg + 8 * idx, Ts + r * CP + 8 * c8);
-        copy8<Arm>(Pg + 8 * idx, Ps + r * CP + 8 * c8);
-      }
-      for (int idx = tid; idx < C * 4; idx += 128) {
-        const int r = idx >> 2, c8 = idx & 3;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (r < L) {
-          if (load8f(p.v, ((t0 + r) * p.hv + h) * (int64_t)DV + 32 * slice + 8 * c8, p.qkv_f32, x))
-            bad |= GDN_ST_NONFINITE_INPUT;
-        }
-        float4* vd = (float4*)(Vs + r * VP + 8 * c8);
-        vd[0] = (float4){x[0], x[1], x[2], x[3]};
-        vd[1] = (float4){x[4], x[5], x[6], x[7]};
-      }
+#pragma unroll
+    for (int j = 0; j < Stage::NV; ++j) {
+      const int idx = ltid + 128 * j, r = idx / (32 / EPC), c = idx % (32 / EPC);
+      const int rr = r < L ? r : L - 1;
+      const int64_t off = (((t0 + rr) * p.hv + h) * (int64_t)DV + 32 * slice + c * EPC) * ESZ;
+      const u32x4 a = ld16(p.v, off);
+      sv[rs][j] = (r < L) ? a : (u32x4)(0u);
     }
-    __syncthreads();
+  };
 
-    // ---- chunk step for this wave's 16 state columns
+  // ---- loaders: register set `rs` -> LDS buffer, plus the in-chunk gate sweep
+  auto commit = [&](int rs, const Buf& B) __attribute__((always_inline)) {
+    if constexpr (!KDA) {
+#pragma unroll
+      for (int j = 0; j < Stage::NKQ; ++j) {
+        const int idx = ltid + 128 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
+        put16<Arm, QF32>(sk[rs][j], B.Ks + r * KP + c * EPC);
+        put16<Arm, QF32>(sq[rs][j], B.Qs + r * KP + c * EPC);
+      }
+      if (u == 0) {
+        const float G = wave_prefix_sum(sg[rs], lane);
+        const float GC = __shfl(G, C - 1, 64);
+        if (lane < C) {
+          const float eg = nexp(G);
+          B.sb_[lane] = sbt[rs];
+          B.sbe[lane] = sbt[rs] * eg;
+          B.seg[lane] = eg;
+          B.sel[lane] = nexp(GC - G);
+        }
+        if (lane == 0) B.sdec[0] = nexp(GC);
+      }
+    } else {
+      if (u == 0 && lane < C) B.sb_[lane] = sbt[rs];
+      if (ltid < DK) B.sdec[ltid] = sdc[rs];
+#pragma unroll
+      for (int j = 0; j < Stage::NG; ++j) {
+        const int e0 = (ltid + 128 * j) * EPT, m = e0 / (C * DK), r = (e0 / DK) % C, c = e0 % DK;
+        *(u32x4*)(B.Ks + (m * C + r) * KP + c) = skg[rs][j];  // Ks, Kl, Qs are consecutive
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < Stage::NTP; ++j) {
+      const int e0 = (ltid + 128 * j) * EPT, r = e0 / C, c = e0 % C;
+      *(u32x4*)(B.Ts + r * CP + c) = stt[rs][j];
+      *(u32x4*)(B.Ps + r * CP + c) = spp[rs][j];
+    }
+#pragma unroll
+    for (int j = 0; j < Stage::NV; ++j) {
+      const int idx = ltid + 128 * j, r = idx / (32 / EPC), c = idx % (32 / EPC);
+      if (nonfinite16<QF32>(sv[rs][j])) bad |= GDN_ST_NONFINITE_INPUT;
+      put16f<QF32>(sv[rs][j], B.Vs + r * VP + c * EPC);
+    }
+  };
+
+  // compute waves: fp32 state of this wave's 16 columns, rows d = 16 t + 4 g + ii
+  f32x4 H[NTK];
+  const int64_t hbase = ((int64_t)n * p.hv + h) * DK * (int64_t)DV;
+
+  // ---- compute waves: one chunk for this wave's 16 state columns.  Each phase's LDS
+  //      fragments are read into registers before its matrix products (the scheduling
+  //      barriers keep the reads batched), and the output products that do not depend
+  //      on the state chain fill the chain's dependency gaps.
+  auto compute = [&](const Buf& B, int64_t ci) __attribute__((always_inline)) {
+    const int64_t t0 = s0 + ci * C;
+    const int L = (int)min64(C, s1 - t0);
     F HB[NBK];
 #pragma unroll
     for (int kb = 0; kb < NBK; ++kb) HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
 
-    // Y = K H ;  X = beta V - beta e^{G} Y   (rows r = 16 mt + 4 g + ii)
+    // K and Q fragments
+    F kf[NBK][NT], qf[NBK][NT];
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const T* krow = B.Ks + (16 * mt + i) * KP + 32 * kb + 4 * g;
+        kf[kb][mt] = Arm::row(krow, krow + 16);
+      }
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const T* qrow = B.Qs + (16 * nt + i) * KP + 32 * kb + 4 * g;
+        qf[kb][nt] = Arm::row(qrow, qrow + 16);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Y = K H_in (row tiles are independent accumulators, interleaved per k-block)
+    f32x4 Y[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) Y[mt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
+
+    // T fragments (lower triangle only) while O^T = H_in^T Q^T runs
+    F tf[NBC][NT];
+#pragma unroll
+    for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+        if (32 * sb <= 16 * mt + 15) {
+          const T* trow = B.Ts + (16 * mt + i) * CP + 32 * sb + 4 * g;
+          tf[sb][mt] = Arm::row(trow, trow + 16);
+        }
+    f32x4 O[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) O[nt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[nt] = Arm::mma(HB[kb], qf[kb][nt], O[nt]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // X = beta V - beta e^{G} Y   (rows r = 16 mt + 4 g + ii)
     f32x4 X[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
-      f32x4 y = zero4();
-      const T* krow = Ks + (16 * mt + i) * KP;
-#pragma unroll
-      for (int kb = 0; kb < NBK; ++kb)
-        y = Arm::mma(Arm::row(krow + 32 * kb + 4 * g, krow + 32 * kb + 16 + 4 * g), HB[kb], y);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * mt + 4 * g + ii;
-        const float ys = KDA ? y[ii] : sbe[r] * y[ii];
-        X[mt][ii] = sb_[r] * Vs[r * VP + 16 * u + i] - ys;
+        // per-channel gate: K already carries e^{G}, beta applies to the whole row
+        X[mt][ii] = KDA ? B.sb_[r] * (B.Vs[r * VP + 16 * u + i] - Y[mt][ii])
+                        : B.sb_[r] * B.Vs[r * VP + 16 * u + i] - B.sbe[r] * Y[mt][ii];
       }
     }
     F XB[NBC];
 #pragma unroll
     for (int sb = 0; sb < NBC; ++sb) XB[sb] = Arm::acc(X[2 * sb], X[2 * sb + 1]);
 
-    // R = T X   (T lower triangular: s-blocks above the row tile are skipped)
+    // R = T X
     f32x4 R[NT];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      R[mt] = zero4();
-      const T* trow = Ts + (16 * mt + i) * CP;
+    for (int mt = 0; mt < NT; ++mt) R[mt] = zero4();
 #pragma unroll
-      for (int sb = 0; sb < NBC; ++sb)
-        if (32 * sb <= 16 * mt + 15)
-          R[mt] = Arm::mma(Arm::row(trow + 32 * sb + 4 * g, trow + 32 * sb + 16 + 4 * g), XB[sb], R[mt]);
-    }
+    for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+        if (32 * sb <= 16 * mt + 15) R[mt] = Arm::mma(tf[sb][mt], XB[sb], R[mt]);
+
+    // Ktil^T fragments (transposing LDS reads) and P fragments
+    F ktf[NBC][NTK], pf[NBC][NT];
+#pragma unroll
+    for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+      for (int t = 0; t < NTK; ++t) ktf[sb][t] = Arm::col(B.Kl, KP, 32 * sb, 16 * t, lane);
+#pragma unroll
+    for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (32 * sb <= 16 * nt + 15) {
+          const T* prow = B.Ps + (16 * nt + i) * CP + 32 * sb + 4 * g;
+          pf[sb][nt] = Arm::row(prow, prow + 16);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+
     F RO[NBC], RS[NBC];
 #pragma unroll
     for (int sb = 0; sb < NBC; ++sb) {
@@ -793,32 +982,42 @@ __global__ __launch_bounds__(128) void gdn_scan(Params p) {
         f32x4 lo, hi;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          lo[ii] = sel[32 * sb + 4 * g + ii] * R[2 * sb][ii];
-          hi[ii] = sel[32 * sb + 16 + 4 * g + ii] * R[2 * sb + 1][ii];
+          lo[ii] = B.sel[32 * sb + 4 * g + ii] * R[2 * sb][ii];
+          hi[ii] = B.sel[32 * sb + 16 + 4 * g + ii] * R[2 * sb + 1][ii];
         }
         RS[sb] = Arm::acc(lo, hi);
       }
     }
 
-    // O^T = H^T (Q e^{G})^T + R^T P^T: lane holds 4 consecutive value columns of one row
+    // H <- e^{G_C} H + Ktil^T R
+#pragma unroll
+    for (int t = 0; t < NTK; ++t) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) H[t][ii] *= KDA ? B.sdec[16 * t + 4 * g + ii] : B.sdec[0];
+    }
+#pragma unroll
+    for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+      for (int t = 0; t < NTK; ++t) H[t] = Arm::mma(ktf[sb][t], RS[sb], H[t]);
+
+    // O^T: gate scaling of the H_in part, then + R^T P^T
+    if constexpr (!KDA) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float e = B.seg[16 * nt + i];
+        O[nt][0] *= e; O[nt][1] *= e; O[nt][2] *= e; O[nt][3] *= e;
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (32 * sb <= 16 * nt + 15) O[nt] = Arm::mma(RO[sb], pf[sb][nt], O[nt]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 o = zero4();
-      const T* qrow = Qs + (16 * nt + i) * KP;
-#pragma unroll
-      for (int kb = 0; kb < NBK; ++kb)
-        o = Arm::mma(HB[kb], Arm::row(qrow + 32 * kb + 4 * g, qrow + 32 * kb + 16 + 4 * g), o);
       const int r = 16 * nt + i;
-      if constexpr (!KDA) {
-        const float e = seg[r];
-        o[0] *= e; o[1] *= e; o[2] *= e; o[3] *= e;
-      }
-      const T* prow = Ps + r * CP;
-#pragma unroll
-      for (int sb = 0; sb < NBC; ++sb)
-        if (32 * sb <= 16 * nt + 15)
-          o = Arm::mma(RO[sb], Arm::row(prow + 32 * sb + 4 * g, prow + 32 * sb + 16 + 4 * g), o);
       if (r < L) {
+        const f32x4 o = O[nt];
         if (f_nonfinite(o[0]) || f_nonfinite(o[1]) || f_nonfinite(o[2]) || f_nonfinite(o[3]))
           bad |= GDN_ST_NONFINITE_OUTPUT;
         const int64_t e = ((t0 + r) * p.hv + h) * (int64_t)DV + col0 + 4 * g;
@@ -831,26 +1030,83 @@ __global__ __launch_bounds__(128) void gdn_scan(Params p) {
         }
       }
     }
+  };
 
-    // H <- e^{G_C} H + Ktil^T R   (Ktil^T read through the transposing LDS path)
-#pragma unroll
-    for (int t = 0; t < NTK; ++t) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) H[t][ii] *= KDA ? sdec[16 * t + 4 * g + ii] : sdec[0];
-#pragma unroll
-      for (int sb = 0; sb < NBC; ++sb) H[t] = Arm::mma(Arm::col(Kl, KP, 32 * sb, 16 * t, lane), RS[sb], H[t]);
+  // ---- pipeline.  Each role runs its own loop (so the loaders' staging registers and
+  //      the compute waves' state never have to be live at the same time); both loops
+  //      execute the same sequence of barriers.  While the compute waves work on chunk ci
+  //      (LDS buffer ci&1), the loaders commit chunk ci+1 (register set (ci+1)&1, loaded
+  //      two chunks earlier) into the other buffer and start loading chunk ci+3 into the
+  //      set they just emptied.  Loops are unrolled by two so that buffer and register-set
+  //      indices are compile-time constants.
+  if (loader) {
+    if (nch > 0) {
+      issue(0, 0);
+      if (nch > 1) issue(1, 1);
+      commit(0, buf_at(0));
+      if (nch > 2) issue(0, 2);
     }
     __syncthreads();
-  }
-
-  if (p.hT) {
+    auto lstep = [&](auto PAR, int64_t ci) __attribute__((always_inline)) {
+      constexpr int par = decltype(PAR)::value;  // ci & 1
+      constexpr int cur = NBUF == 2 ? par : 0;
+      constexpr int rs = par ^ 1;                // register set holding chunk ci+1
+      if (NBUF == 2) {
+        if (ci + 1 < nch) {
+          commit(rs, buf_at(cur ^ 1));
+          if (ci + 3 < nch) issue(rs, ci + 3);
+        }
+        __syncthreads();
+      } else {
+        __syncthreads();
+        if (ci + 1 < nch) {
+          commit(rs, buf_at(0));
+          if (ci + 3 < nch) issue(rs, ci + 3);
+          __syncthreads();
+        }
+      }
+    };
+    for (int64_t ci = 0; ci < nch; ci += 2) {
+      lstep(std::integral_constant<int, 0>{}, ci);
+      if (ci + 1 < nch) lstep(std::integral_constant<int, 1>{}, ci + 1);
+    }
+  } else {
+    // ---- compute waves: initial state
+    if (p.h0) {
 #pragma unroll
-    for (int t = 0; t < NTK; ++t) {
+      for (int t = 0; t < NTK; ++t)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int d = 16 * t + 4 * g + ii;
-        if (f_nonfinite(H[t][ii])) bad |= GDN_ST_NONFINITE_OUTPUT;
-        p.hT[hbase + (int64_t)d * DV + col0 + i] = H[t][ii];
+        for (int ii = 0; ii < 4; ++ii) H[t][ii] = p.h0[hbase + (int64_t)(16 * t + 4 * g + ii) * DV + col0 + i];
+#pragma unroll
+      for (int t = 0; t < NTK; ++t)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (f_nonfinite(H[t][ii])) bad |= GDN_ST_NONFINITE_INPUT;
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTK; ++t) H[t] = zero4();
+    }
+    __syncthreads();
+    auto cstep = [&](auto PAR, int64_t ci) __attribute__((always_inline)) {
+      constexpr int par = decltype(PAR)::value;
+      constexpr int cur = NBUF == 2 ? par : 0;
+      compute(buf_at(cur), ci);
+      __syncthreads();
+      if (NBUF == 1 && ci + 1 < nch) __syncthreads();
+    };
+    for (int64_t ci = 0; ci < nch; ci += 2) {
+      cstep(std::integral_constant<int, 0>{}, ci);
+      if (ci + 1 < nch) cstep(std::integral_constant<int, 1>{}, ci + 1);
+    }
+    if (p.hT) {
+#pragma unroll
+      for (int t = 0; t < NTK; ++t) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int d = 16 * t + 4 * g + ii;
+          if (f_nonfinite(H[t][ii])) bad |= GDN_ST_NONFINITE_OUTPUT;
+          p.hT[hbase + (int64_t)d * DV + col0 + i] = H[t][ii];
+        }
       }
     }
   }
@@ -858,42 +1114,60 @@ __global__ __launch_bounds__(128) void gdn_scan(Params p) {
 }
 
 // ------------------------------------------------------------ launch -----
-template <class Arm, int DK, int C, bool KDA>
+// Kernel attributes are set once per instantiation (the first launch); later launches
+// reuse them.
+template <class Fn>
+bool set_lds_once(Fn fn, size_t lds) {
+  static bool done = false;
+  if (!done) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+        hipSuccess)
+      return false;
+    done = true;
+  }
+  return true;
+}
+
+template <class Arm, int DK, int C, bool KDA, bool QF32>
 gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
-  if (pl.max_slots > 0) {
+  if (pl.run_prep && pl.max_slots > 0) {
     const size_t lds = prep_lds_bytes<Arm, DK, C>(KDA);
-    const void* fn = (const void*)gdn_prep<Arm, DK, C, KDA>;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return GDN_E_LAUNCH;
+    if (!set_lds_once(gdn_prep<Arm, DK, C, KDA, QF32>, lds)) return GDN_E_LAUNCH;
     const int64_t blocks = pl.max_slots * (KDA ? pl.hv : pl.hk);
-    hipLaunchKernelGGL((gdn_prep<Arm, DK, C, KDA>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+    hipLaunchKernelGGL((gdn_prep<Arm, DK, C, KDA, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
-  {
+  if (pl.run_scan) {
     const size_t lds = scan_lds_bytes<Arm, DK, C>(KDA);
-    const void* fn = (const void*)gdn_scan<Arm, DK, C, KDA>;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return GDN_E_LAUNCH;
+    if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32>, lds)) return GDN_E_LAUNCH;
     const int64_t blocks = (int64_t)pl.n_seq * pl.hv * (pl.dv / 32);
-    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA>), dim3((unsigned)blocks), dim3(128), lds, st, prm);
+    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   return GDN_OK;
 }
 
-template <class Arm, int DK>
+template <class Arm, int DK, bool QF32>
 gdn_status run_dk(const Plan& pl, const Params& prm, hipStream_t st) {
-  if (pl.gate_channel) return run<Arm, DK, 32, true>(pl, prm, st);
-  if (pl.chunk == 32) return run<Arm, DK, 32, false>(pl, prm, st);
-  return run<Arm, DK, 64, false>(pl, prm, st);
+  if (pl.gate_channel) return run<Arm, DK, 32, true, QF32>(pl, prm, st);
+  if (pl.chunk == 32) return run<Arm, DK, 32, false, QF32>(pl, prm, st);
+  return run<Arm, DK, 64, false, QF32>(pl, prm, st);
 }
 
 template <class Arm>
 gdn_status run_arm(const Plan& pl, const Params& prm, hipStream_t st) {
+  if (pl.qkv_f32) {
+    switch (pl.dk) {
+      case 32: return run_dk<Arm, 32, true>(pl, prm, st);
+      case 64: return run_dk<Arm, 64, true>(pl, prm, st);
+      case 128: return run_dk<Arm, 128, true>(pl, prm, st);
+      default: return GDN_E_UNSUPPORTED;
+    }
+  }
   switch (pl.dk) {
-    case 32: return run_dk<Arm, 32>(pl, prm, st);
-    case 64: return run_dk<Arm, 64>(pl, prm, st);
-    case 128: return run_dk<Arm, 128>(pl, prm, st);
+    case 32: return run_dk<Arm, 32, false>(pl, prm, st);
+    case 64: return run_dk<Arm, 64, false>(pl, prm, st);
+    case 128: return run_dk<Arm, 128, false>(pl, prm, st);
     default: return GDN_E_UNSUPPORTED;
   }
 }
@@ -902,7 +1176,7 @@ gdn_status run_arm(const Plan& pl, const Params& prm, hipStream_t st) {
 
 gdn_status launch(const Plan& pl, const Params& prm, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  if (pl.varlen) {
+  if (pl.varlen && pl.run_prep) {
     hipLaunchKernelGGL(gdn_chunk_table, dim3(1), dim3(256), 0, st, prm, (int)pl.chunk);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }

@@ -26,6 +26,7 @@ GATE_HEAD, GATE_KEY_CHANNEL = 0, 1
 BF16, F32 = 0, 1
 ARM_MFMA_BF16, ARM_FOLD_F32 = 0, 1
 COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED = 0, 1, 2
+STAGE_ALL, STAGE_PREP, STAGE_SCAN = 0, 1, 2
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_chunk_fwd", "gdn_error_string",
@@ -37,7 +38,8 @@ class Problem(ctypes.Structure):
                 ("seq_len", ctypes.c_int32), ("hk", ctypes.c_int32), ("hv", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
-                ("o_dtype", ctypes.c_int32), ("arm", ctypes.c_int32), ("compose", ctypes.c_int32)]
+                ("o_dtype", ctypes.c_int32), ("arm", ctypes.c_int32), ("compose", ctypes.c_int32),
+                ("stages", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -99,9 +101,11 @@ def abi_version() -> int:
 
 
 def make_problem(n_seq, total_tokens, seq_len, hk, hv, dk, dv, gate=GATE_HEAD, chunk=0,
-                 qkv_dtype=BF16, o_dtype=BF16, arm=ARM_MFMA_BF16, compose=COMPOSE_AUTO) -> Problem:
+                 qkv_dtype=BF16, o_dtype=BF16, arm=ARM_MFMA_BF16, compose=COMPOSE_AUTO,
+                 stages=STAGE_ALL) -> Problem:
     return Problem(int(n_seq), int(total_tokens), int(seq_len), int(hk), int(hv), int(dk), int(dv),
-                   int(gate), int(chunk), int(qkv_dtype), int(o_dtype), int(arm), int(compose))
+                   int(gate), int(chunk), int(qkv_dtype), int(o_dtype), int(arm), int(compose),
+                   int(stages))
 
 
 def validate(prob: Problem) -> int:

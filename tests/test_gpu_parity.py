@@ -73,3 +73,32 @@ def test_fp32_inputs_and_outputs(arm):
 
 def test_single_sequence_config():
     _check(inputs.make("single"), "bf16")
+
+
+def test_stage_calls_equal_one_full_call_bitwise():
+    """PREP then SCAN on one workspace is the same work as one call: same bits."""
+    import ctypes
+    from linear_attention_rnn_chunk_amd import gdn
+    from tests.gpu_util import device_inputs
+    spec = inputs.Spec("stages", (64, 100, 7), 2, 4, 128, 128, qkv_dtype="bf16", gate_law="half",
+                       h0=True, chunk=64, packed=True, seed=3)
+    inp = inputs.make(spec)
+    d = device_inputs(inp)
+    outs = []
+    for stages_list in ([gdn.STAGE_ALL], [gdn.STAGE_PREP, gdn.STAGE_SCAN]):
+        o = torch.empty((1, spec.tokens, spec.hv, spec.dv), dtype=torch.bfloat16, device="cuda")
+        hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device="cuda")
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ws = None
+        for stages in stages_list:
+            prob = gdn.make_problem(spec.n_seq, spec.tokens, 0, spec.hk, spec.hv, spec.dk, spec.dv,
+                                    gdn.GATE_HEAD, 64, gdn.BF16, gdn.BF16, gdn.ARM_MFMA_BF16,
+                                    gdn.COMPOSE_SPLIT, stages)
+            if ws is None:
+                ws = torch.empty(gdn.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+            assert gdn.chunk_fwd_raw(prob, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                     d["cu_seqlens"], o, hT, st, ws) == gdn.GDN_OK
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        outs.append((o.clone(), hT.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
