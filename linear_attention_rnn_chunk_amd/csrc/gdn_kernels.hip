@@ -728,7 +728,16 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
   const int u = wave & 1;            // compute: state unit; loader: loader index
   const int ltid = tid & 127;        // loader thread index 0..127
   const int DV = p.dv, nslice = DV / 32;
-  int bid = blockIdx.x;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  Give
+  // each XCD a contiguous range of (sequence, value head, slice) work items, so that the
+  // workgroups reading the same key head -- and the 4 slices of one value head -- share
+  // an L2 and hit in it.
+  int bid;
+  {
+    const int nb = (int)gridDim.x, per = nb / 8, rem = nb % 8;
+    const int x = (int)blockIdx.x % 8, pos = (int)blockIdx.x / 8;
+    bid = x * per + (x < rem ? x : rem) + pos;
+  }
   const int slice = bid % nslice;
   bid /= nslice;
   const int h = bid % p.hv;
@@ -778,19 +787,40 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
 
   // ---- loaders: global -> register set `rs` for chunk ci (branch-free: rows past the
   //      chunk end re-read its last row, in bounds, and are zeroed by a select)
+  // Per-thread byte offsets inside a chunk (fixed), so that each load is a uniform chunk
+  // base plus a 32-bit offset.  Per-head gate: K/Q rows and V columns of this slice.
+  constexpr int KPR = DK / EPC;  // 16-byte pieces per K row
+  constexpr int VPR = 32 / EPC;  // 16-byte pieces per row of the 32 V columns
+  const int kstride = p.hk * DK * ESZ, vstride = p.hv * DV * ESZ;
+  const uint32_t koff0 = (uint32_t)((ltid / KPR) * kstride + (ltid % KPR) * 16);
+  const uint32_t voff0 = (uint32_t)((ltid / VPR) * vstride + (ltid % VPR) * 16);
+
+  // ---- loaders: global -> register set `rs` for chunk ci.  A partial last chunk reads
+  //      its last row again for the rows past its end (in bounds) and zeroes them.
   auto issue = [&](int rs, int64_t ci) __attribute__((always_inline)) {
     const int64_t t0 = s0 + ci * C;
     const int L = (int)min64(C, s1 - t0);
     const int64_t slot = slot0 + ci;
+    const bool full = L == C;  // uniform
     if constexpr (!KDA) {
+      const char* kb = (const char*)p.k + (t0 * p.hk + kh) * (int64_t)(DK * ESZ);
+      const char* qb = (const char*)p.q + (t0 * p.hk + kh) * (int64_t)(DK * ESZ);
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < Stage::NKQ; ++j) {
-        const int idx = ltid + 128 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
-        const int rr = r < L ? r : L - 1;
-        const int64_t off = (((t0 + rr) * p.hk + kh) * (int64_t)DK + c * EPC) * ESZ;
-        const u32x4 a = ld16(p.k, off), b = ld16(p.q, off);
-        sk[rs][j] = (r < L) ? a : (u32x4)(0u);
-        sq[rs][j] = (r < L) ? b : (u32x4)(0u);
+        for (int j = 0; j < Stage::NKQ; ++j) {
+          const uint32_t off = koff0 + (uint32_t)(j * (128 / KPR) * kstride);
+          sk[rs][j] = *(const u32x4*)(kb + off);
+          sq[rs][j] = *(const u32x4*)(qb + off);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < Stage::NKQ; ++j) {
+          const int r = (ltid + 128 * j) / KPR, c = (ltid + 128 * j) % KPR;
+          const uint32_t off = (uint32_t)((r < L ? r : L - 1) * kstride + c * 16);
+          const u32x4 a = *(const u32x4*)(kb + off), b = *(const u32x4*)(qb + off);
+          sk[rs][j] = (r < L) ? a : (u32x4)(0u);
+          sq[rs][j] = (r < L) ? b : (u32x4)(0u);
+        }
       }
       if (u == 0) {
         const int rr = lane < L ? lane : L - 1;
@@ -815,13 +845,18 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       stt[rs][j] = Tg[ltid + 128 * j];
       spp[rs][j] = Pg[ltid + 128 * j];
     }
+    const char* vb = (const char*)p.v + (t0 * p.hv + h) * (int64_t)(DV * ESZ) + 32 * slice * ESZ;
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < Stage::NV; ++j) {
-      const int idx = ltid + 128 * j, r = idx / (32 / EPC), c = idx % (32 / EPC);
-      const int rr = r < L ? r : L - 1;
-      const int64_t off = (((t0 + rr) * p.hv + h) * (int64_t)DV + 32 * slice + c * EPC) * ESZ;
-      const u32x4 a = ld16(p.v, off);
-      sv[rs][j] = (r < L) ? a : (u32x4)(0u);
+      for (int j = 0; j < Stage::NV; ++j)
+        sv[rs][j] = *(const u32x4*)(vb + voff0 + (uint32_t)(j * (128 / VPR) * vstride));
+    } else {
+#pragma unroll
+      for (int j = 0; j < Stage::NV; ++j) {
+        const int r = (ltid + 128 * j) / VPR, c = (ltid + 128 * j) % VPR;
+        const u32x4 a = *(const u32x4*)(vb + (uint32_t)((r < L ? r : L - 1) * vstride + c * 16));
+        sv[rs][j] = (r < L) ? a : (u32x4)(0u);
+      }
     }
   };
 
