@@ -64,3 +64,50 @@ def rel(x, ref):
         return float("inf")
     den = np.linalg.norm(ref.ravel())
     return float(np.linalg.norm((x - ref).ravel()) / den) if den > 0 else float(np.linalg.norm(x.ravel()))
+
+
+def oracle_units(inp, units, want_o=True):
+    """fp64 oracle on selected (sequence, value head) units only; returns
+    {(n, h): (o [len, dv] or None, hT [dk, dv])}.  Each unit becomes one sequence of a
+    packed single-head problem (its key head's q/k, its value head's v/g/beta, its h0),
+    so large workloads stay cheap and the units run in parallel."""
+    spec = inp.spec
+    group = spec.hv // spec.hk
+    cu = inp.cu_seqlens
+    q32, k32, v32 = inp.as_f32("q"), inp.as_f32("k"), inp.as_f32("v")
+    qs, ks, vs, gs, bs, h0s, starts = [], [], [], [], [], [], [0]
+    for n, h in units:
+        kh = h // group
+        sl = slice(int(cu[n]), int(cu[n + 1]))
+        qs.append(q32[sl, kh:kh + 1])
+        ks.append(k32[sl, kh:kh + 1])
+        vs.append(v32[sl, h:h + 1])
+        gs.append(inp.g[sl, h:h + 1])
+        bs.append(inp.beta[sl, h:h + 1])
+        h0s.append(np.zeros((1, spec.dk, spec.dv)) if inp.h0 is None else inp.h0[n, h:h + 1])
+        starts.append(starts[-1] + (sl.stop - sl.start))
+    cat = lambda xs: np.concatenate(xs).astype(np.float64)
+    o, hT = oracle.serial_fwd(cat(qs), cat(ks), cat(vs), cat(gs), cat(bs),
+                              np.stack(h0s).astype(np.float64), seq_start=np.array(starts),
+                              want_o=want_o)
+    out = {}
+    for i, u in enumerate(units):
+        out[tuple(u)] = (None if o is None else o[starts[i]:starts[i + 1], 0], hT[i, 0])
+    return out
+
+
+def workspace_tile_views(prob, ws, arm_f32):
+    """T and P tiles inside the library's workspace for a fixed-length problem
+    (layout: T tiles [slot][hv][C][C], then P tiles, each region 256-byte aligned)."""
+    import torch
+    C = prob.chunk
+    esz = 4 if arm_f32 else 2
+    cps = (prob.seq_len + C - 1) // C
+    slots = prob.n_seq * cps
+    n = slots * prob.hv * C * C
+    tile_bytes = n * esz
+    off_p = (tile_bytes + 255) // 256 * 256
+    dt = torch.float32 if arm_f32 else torch.bfloat16
+    T = ws[:tile_bytes].view(dt).view(slots, prob.hv, C, C)
+    P = ws[off_p:off_p + tile_bytes].view(dt).view(slots, prob.hv, C, C)
+    return T, P
