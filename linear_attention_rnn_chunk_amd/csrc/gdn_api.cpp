@@ -62,15 +62,14 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
     pl.max_slots = (int64_t)p->n_seq * pl.chunks_per_seq;
   }
   // grid sizes are flattened into blockIdx.x
-  const int64_t heads_prep = pl.gate_channel ? pl.hv : pl.hk;
-  if (pl.max_slots * heads_prep > INT32_MAX) return GDN_E_UNSUPPORTED;
+  if (pl.max_slots * pl.hv > INT32_MAX) return GDN_E_UNSUPPORTED;
   if ((int64_t)pl.n_seq * pl.hv * (pl.dv / 32) > INT32_MAX) return GDN_E_UNSUPPORTED;
 
   const size_t esz = pl.arm_f32 ? 4 : 2;
   size_t off = 0;
   pl.off_table = off;
   off = round_up(off + (pl.varlen ? 2 * sizeof(int32_t) * (size_t)(pl.n_seq + 1) : 0), 256);
-  const size_t tile = (size_t)pl.max_slots * pl.hv * C * C * esz;
+  const size_t tile = (size_t)pl.max_slots * pl.hv * gdn::tile_elems(C) * esz;
   pl.off_T = off;
   off = round_up(off + tile, 256);
   pl.off_P = off;

@@ -7,6 +7,18 @@
 
 namespace gdn {
 
+// T and P of a chunk are stored as the scan's MFMA operand fragments: fragment (mt, sb)
+// of a C x C lower-triangular tile covers rows 16 mt .. 16 mt + 15 and columns
+// 32 sb .. 32 sb + 31, 64 lanes x 8 elements; only those with sb <= mt / 2 (touching
+// the lower triangle) exist, in this order.
+constexpr int tile_frag_index(int mt, int sb) {
+  int f = 0;
+  for (int m = 0; m < mt; ++m) f += (m >> 1) + 1;
+  return f + sb;
+}
+constexpr int tile_frags(int C) { return tile_frag_index(C / 16, 0); }
+constexpr int tile_elems(int C) { return tile_frags(C) * 512; }
+
 // Everything a launch needs, resolved on the host from a gdn_problem.
 struct Plan {
   int32_t n_seq, seq_len, hk, hv, dk, dv;
@@ -37,8 +49,8 @@ struct Params {
   float* hT;
   uint32_t* status;
   int32_t* table;  // varlen: [n_seq+1] sanitised bounds, then [n_seq+1] chunk prefix
-  void* Tws;       // [slot][hv][C][C] solved T (arm element type)
-  void* Pws;       // [slot][hv][C][C] masked P (arm element type)
+  void* Tws;       // [slot][hv][tile_elems(C)] solved T fragments (arm element type)
+  void* Pws;       // [slot][hv][tile_elems(C)] masked P fragments (arm element type)
   void* Gws;       // per-channel gate: [slot][hv][3][C][dk] e^{G} K, e^{G_C-G} K, e^{G} Q
   float* Dws;      // per-channel gate: [slot][hv][dk] e^{G_C}
   int64_t total;

@@ -55,10 +55,32 @@ __device__ __forceinline__ float nexp(float x) { return __builtin_amdgcn_exp2f(x
 
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
-__device__ __forceinline__ bool bf_nonfinite(uint32_t two) {  // either half is Inf/NaN
-  return ((two & 0x7F80u) == 0x7F80u) || ((two & 0x7F800000u) == 0x7F800000u);
+// Inf/NaN tests as bit arithmetic: no short-circuit branches, so loads around them
+// can still be issued back to back.
+__device__ __forceinline__ uint32_t nf_f32(uint32_t u) { return (u & 0x7F800000u) == 0x7F800000u; }
+__device__ __forceinline__ uint32_t nf_bf16x2(uint32_t two) {  // either half is Inf/NaN
+  return (uint32_t)((two & 0x7F80u) == 0x7F80u) | (uint32_t)((two & 0x7F800000u) == 0x7F800000u);
 }
-__device__ __forceinline__ bool f_nonfinite(float x) { return !__builtin_isfinite(x); }
+__device__ __forceinline__ uint32_t f_nonfinite(float x) { return nf_f32(__float_as_uint(x)); }
+// Inf/NaN accumulation for raw 16-byte input pieces: the returned word has bit 15 or 31
+// (bf16) / bit 31 (fp32) set when some element's exponent field is all ones (adding one
+// unit to a saturated exponent field carries into the bit above it).
+template <bool QF32>
+__device__ __forceinline__ uint32_t nf_bits16(u32x4 a) {
+  if constexpr (QF32) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m |= (a[j] & 0x7F800000u) + 0x00800000u;  // bit 31
+    return m & 0x80000000u;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m |= (a[j] & 0x7F807F80u) + 0x00800080u;  // bits 15, 31
+    return m & 0x80008000u;
+  }
+}
+// `flag` when `c` is nonzero, else 0
+__device__ __forceinline__ uint32_t flag_if(uint32_t c, uint32_t flag) { return c ? flag : 0u; }
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -116,6 +138,18 @@ struct ArmBF16 {
   __device__ static __forceinline__ f32x4 mma(const F& a, const F& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  // 8 bf16 input elements (16 bytes) as a fragment
+  __device__ static __forceinline__ F from_bf16(u32x4 a) { return __builtin_bit_cast(F, a); }
+  __device__ static __forceinline__ F from_f32(const float* x) {
+    F f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (__bf16)x[j];
+    return f;
+  }
+  // 8 consecutive elements (16-byte aligned) as a fragment
+  __device__ static __forceinline__ F ld8(const T* p) { return *(const F*)p; }
+  // 8 fp32 values (lo then hi) stored as 8 consecutive elements
+  __device__ static __forceinline__ void st8(T* p, f32x4 lo, f32x4 hi) { *(F*)p = acc(lo, hi); }
 };
 
 // fp32 MFMA operands (v_mfma_f32_16x16x4_f32, eight per K = 32 fragment).
@@ -134,13 +168,6 @@ struct ArmF32 {
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
     return f;
   }
-  __device__ static __forceinline__ F row_half(const T* p0) {
-    const float4 a = *(const float4*)p0;
-    F f;
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = 0.f; f.v[5] = 0.f; f.v[6] = 0.f; f.v[7] = 0.f;
-    return f;
-  }
   __device__ static __forceinline__ F col(const T* base, int pitch, int k0, int n0, int lane) {
     const int i = lane & 15, g = lane >> 4;
     F f;
@@ -151,26 +178,10 @@ struct ArmF32 {
     }
     return f;
   }
-  __device__ static __forceinline__ F col_half(const T* base, int pitch, int k0, int n0, int lane) {
-    const int i = lane & 15, g = lane >> 4;
-    F f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f.v[j] = base[(k0 + 4 * g + j) * pitch + n0 + i];
-      f.v[4 + j] = 0.f;
-    }
-    return f;
-  }
   __device__ static __forceinline__ F acc(f32x4 lo, f32x4 hi) {
     F f;
     f.v[0] = lo[0]; f.v[1] = lo[1]; f.v[2] = lo[2]; f.v[3] = lo[3];
     f.v[4] = hi[0]; f.v[5] = hi[1]; f.v[6] = hi[2]; f.v[7] = hi[3];
-    return f;
-  }
-  __device__ static __forceinline__ F acc_half(f32x4 lo) {
-    F f;
-    f.v[0] = lo[0]; f.v[1] = lo[1]; f.v[2] = lo[2]; f.v[3] = lo[3];
-    f.v[4] = 0.f; f.v[5] = 0.f; f.v[6] = 0.f; f.v[7] = 0.f;
     return f;
   }
   __device__ static __forceinline__ f32x4 mma(const F& a, const F& b, f32x4 c) {
@@ -178,92 +189,38 @@ struct ArmF32 {
     for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
     return c;
   }
+  __device__ static __forceinline__ F from_bf16(u32x4 a) {
+    F f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[2 * j] = __uint_as_float(a[j] << 16);
+      f.v[2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+    }
+    return f;
+  }
+  __device__ static __forceinline__ F from_f32(const float* x) {
+    F f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+    return f;
+  }
+  __device__ static __forceinline__ F ld8(const T* p) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    F f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+  __device__ static __forceinline__ void st8(T* p, f32x4 lo, f32x4 hi) {
+    *(float4*)p = (float4){lo[0], lo[1], lo[2], lo[3]};
+    *(float4*)(p + 4) = (float4){hi[0], hi[1], hi[2], hi[3]};
+  }
 };
 
 // ------------------------------------------------------ global I/O -------
-// 8 consecutive input elements (bf16 or fp32 per flag) into 8 LDS elements of the arm.
-// Returns true when any of them is not finite.
-template <class Arm>
-__device__ __forceinline__ bool load8(const void* src, int64_t e, int src_f32, typename Arm::T* dst) {
-  bool bad = false;
-  if (src_f32) {
-    const float4* s = (const float4*)((const float*)src + e);
-    const float4 a = s[0], b = s[1];
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bad |= f_nonfinite(x[j]);
-    if constexpr (sizeof(typename Arm::T) == 4) {
-      float4* d = (float4*)dst;
-      d[0] = a;
-      d[1] = b;
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f2bf(x[2 * j]) | ((uint32_t)f2bf(x[2 * j + 1]) << 16);
-      *(uint4*)dst = (uint4){w[0], w[1], w[2], w[3]};
-    }
-  } else {
-    const uint4 a = *(const uint4*)((const uint16_t*)src + e);
-    bad = bf_nonfinite(a.x) || bf_nonfinite(a.y) || bf_nonfinite(a.z) || bf_nonfinite(a.w);
-    if constexpr (sizeof(typename Arm::T) == 4) {
-      float4* d = (float4*)dst;
-      d[0] = (float4){__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
-                      __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
-      d[1] = (float4){__uint_as_float(a.z << 16), __uint_as_float(a.z & 0xFFFF0000u),
-                      __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xFFFF0000u)};
-    } else {
-      *(uint4*)dst = a;
-    }
-  }
-  return bad;
-}
-
-template <class Arm>
-__device__ __forceinline__ void zero8(typename Arm::T* dst) {
-  if constexpr (sizeof(typename Arm::T) == 4) {
-    ((float4*)dst)[0] = (float4){0.f, 0.f, 0.f, 0.f};
-    ((float4*)dst)[1] = (float4){0.f, 0.f, 0.f, 0.f};
-  } else {
-    *(uint4*)dst = (uint4){0u, 0u, 0u, 0u};
-  }
-}
-
 // one input element as fp32
 __device__ __forceinline__ float load1(const void* src, int64_t e, int src_f32) {
   return src_f32 ? ((const float*)src)[e] : bf2f(((const uint16_t*)src)[e]);
-}
-
-// 8 input elements as fp32 (v rows)
-__device__ __forceinline__ bool load8f(const void* src, int64_t e, int src_f32, float* x) {
-  bool bad = false;
-  if (src_f32) {
-    const float4* s = (const float4*)((const float*)src + e);
-    const float4 a = s[0], b = s[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bad |= f_nonfinite(x[j]);
-  } else {
-    const uint4 a = *(const uint4*)((const uint16_t*)src + e);
-    bad = bf_nonfinite(a.x) || bf_nonfinite(a.y) || bf_nonfinite(a.z) || bf_nonfinite(a.w);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = __uint_as_float(w[j] << 16);
-      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  }
-  return bad;
-}
-
-// 8 arm elements from global (workspace) to LDS
-template <class Arm>
-__device__ __forceinline__ void copy8(const typename Arm::T* src, typename Arm::T* dst) {
-  if constexpr (sizeof(typename Arm::T) == 4) {
-    ((float4*)dst)[0] = ((const float4*)src)[0];
-    ((float4*)dst)[1] = ((const float4*)src)[1];
-  } else {
-    *(uint4*)dst = *(const uint4*)src;
-  }
 }
 
 // Location of a chunk slot: sequence, first token, valid rows.  False for slots past
@@ -354,73 +311,15 @@ __global__ __launch_bounds__(256) void gdn_chunk_table(Params p, int C) {
   if (bad) atomicOr(p.status, GDN_ST_BAD_SEQLENS);
 }
 
-// ---------------------------------------------------- blocked solve ------
-// T = (I + A)^-1 for a strictly lower C x C matrix A (fp32, LDS, pitch C+4):
-// 16 x 16 diagonal blocks by forward substitution (one lane per block column),
-// then the off-diagonal blocks level by level, T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj,
-// on fp32 MFMA (one wave per block of a level).
-template <int C>
-__device__ void solve_unit_lower(const float* Am, float* Tm, int tid) {
-  constexpr int NB = C / 16, AP = C + 4;
-  const int lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx / C, s = idx % C;
-    if ((s >> 4) > (r >> 4)) Tm[r * AP + s] = 0.f;
-  }
-  if (w == 0 && lane < 16 * NB) {
-    const int base = 16 * (lane >> 4), c = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s_ = (r == c) ? 1.f : 0.f;
-      const float* arow = Am + (base + r) * AP + base;
-#pragma unroll
-      for (int s = 0; s < r; ++s) s_ = fmaf(-arow[s], x[s], s_);
-      x[r] = s_;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Tm[(base + r) * AP + base + c] = x[r];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int dist = 1; dist < NB; ++dist) {
-    if (w < NB - dist) {
-      const int ib = w + dist, jb = w;
-      f32x4 z = zero4();
-      for (int m = jb; m < ib; m += 2) {
-        const float* arow = Am + (16 * ib + i) * AP;
-        if (m + 1 < ib) {
-          ArmF32::F a = ArmF32::row(arow + 16 * m + 4 * g, arow + 16 * (m + 1) + 4 * g);
-          ArmF32::F b = ArmF32::col(Tm, AP, 16 * m, 16 * jb, lane);
-          z = ArmF32::mma(a, b, z);
-        } else {
-          ArmF32::F a = ArmF32::row_half(arow + 16 * m + 4 * g);
-          ArmF32::F b = ArmF32::col_half(Tm, AP, 16 * m, 16 * jb, lane);
-          z = ArmF32::mma(a, b, z);
-        }
-      }
-      ArmF32::F a = ArmF32::row_half(Tm + (16 * ib + i) * AP + 16 * ib + 4 * g);
-      f32x4 t = ArmF32::mma(a, ArmF32::acc_half(z), zero4());
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Tm[(16 * ib + 4 * g + ii) * AP + 16 * jb + i] = -t[ii];
-    }
-    __syncthreads();
-  }
-}
-
 // ------------------------------------------------ 16-byte staging -------
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
   return *(const u32x4*)((const char*)base + byte_off);
 }
 
 template <bool QF32>
-__device__ __forceinline__ bool nonfinite16(u32x4 a) {
-  if constexpr (QF32) {
-    return f_nonfinite(__uint_as_float(a.x)) || f_nonfinite(__uint_as_float(a.y)) ||
-           f_nonfinite(__uint_as_float(a.z)) || f_nonfinite(__uint_as_float(a.w));
-  } else {
-    return bf_nonfinite(a.x) || bf_nonfinite(a.y) || bf_nonfinite(a.z) || bf_nonfinite(a.w);
-  }
+__device__ __forceinline__ uint32_t nonfinite16(u32x4 a) {
+  if constexpr (QF32) return nf_f32(a.x) | nf_f32(a.y) | nf_f32(a.z) | nf_f32(a.w);
+  else return nf_bf16x2(a.x) | nf_bf16x2(a.y) | nf_bf16x2(a.z) | nf_bf16x2(a.w);
 }
 
 // 16 input bytes (8 bf16 or 4 fp32) -> the same elements in the arm's LDS type
@@ -461,217 +360,370 @@ __device__ __forceinline__ void put16f(u32x4 a, float* dst) {
   }
 }
 
-// ----------------------------------------------------------- prep -------
-template <class Arm, int DK, int C>
-constexpr size_t prep_lds_bytes(bool kda) {
-  return (size_t)(kda ? 6 : 2) * C * (DK + Arm::PAD) * sizeof(typename Arm::T)  // operands
-         + 2 * (size_t)C * (C + 4) * sizeof(float)                             // A, T (fp32)
-         + (size_t)C * C * sizeof(typename Arm::T)                             // P staging
-         + 2 * (size_t)C * sizeof(float);                                      // G, beta
+// ------------------------------------------------- T and P as fragments --
+// The scan reads T and P only as MFMA operands whose lanes are rows: fragment (mt, sb)
+// gives lane (i, g) row 16 mt + i at columns 32 sb + 4 g + e (e = 0..3) and
+// 32 sb + 16 + 4 g + (e - 4) (e = 4..7).  Only fragments that touch the lower triangle
+// (sb <= mt / 2) exist.  The workspace holds them exactly so -- per (chunk slot, value
+// head) the fragments in tile_frag_index order, 64 lanes x 8 consecutive elements each --
+// so the scan copies them verbatim and each lane reads a fragment with one 16-byte
+// (bf16) LDS read, free of bank conflicts.
+
+// Per-wave LDS of the in-wave solve: the lower 16 x 16 tiles of a C x C fp32 matrix
+// (tile (rt, st) at tri(rt, st), row pitch kTP), then the chunk's G and beta rows.
+constexpr int kTP = 20, kTile = 16 * kTP;
+__host__ __device__ constexpr int tri(int rt, int st) { return rt * (rt + 1) / 2 + st; }
+template <int C>
+struct SolveLds {
+  static constexpr int NT = C / 16, NTRI = NT * (NT + 1) / 2;
+  static constexpr int FLOATS = NTRI * kTile + 2 * C;
+};
+
+// One wave's LDS accesses in program order, complete: data some lanes wrote is then
+// read by others.  (A wave's LDS operations execute in order; this also keeps the
+// compiler from moving accesses across it.)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// T = (I + A)^-1 for the strictly lower fp32 A held in S (lower tiles; the diagonal
+// tiles' upper parts are ignored), in place: afterwards S holds the lower tiles of T.
+//   diagonal 16 x 16 blocks: forward substitution, one lane per column of a block
+//   off-diagonal blocks, block row by block row:
+//     T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj   (fp32 MFMA 16x16x4)
+// Block row i only reads A's row i and T's earlier rows, so T_i* replaces A_i* once
+// the row is done.  One wave, no workgroup barrier.
+template <int C>
+__device__ __forceinline__ void wave_solve_unit_lower(float* S, int lane) {
+  constexpr int NB = C / 16;
+  const int i = lane & 15, g = lane >> 4;
+  {
+    const int b = (lane >> 4) & (NB - 1), c = lane & 15;
+    float* D = S + tri(b, b) * kTile;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int q = 0; 4 * q < r; ++q) {
+        const float4 a = *(const float4*)(D + r * kTP + 4 * q);
+        const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e < r) acc = fmaf(-av[e], x[4 * q + e], acc);
+      }
+      x[r] = acc;
+    }
+    wave_lds_sync();
+    if (lane < 16 * NB) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) D[r * kTP + c] = x[r];
+    }
+    wave_lds_sync();
+  }
+#pragma unroll
+  for (int ib = 1; ib < NB; ++ib) {
+    f32x4 R[NB];
+#pragma unroll
+    for (int jb = 0; jb < ib; ++jb) {
+      // Z = sum_m A_{ib,m} T_{m,jb}: instruction q pairs k = 4 g + q of lane group g
+      f32x4 Z = zero4();
+#pragma unroll
+      for (int m = jb; m < ib; ++m) {
+        const float4 a = *(const float4*)(S + tri(ib, m) * kTile + i * kTP + 4 * g);
+        const float* tm = S + tri(m, jb) * kTile + 4 * g * kTP + i;
+        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, tm[0], Z, 0, 0, 0);
+        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, tm[kTP], Z, 0, 0, 0);
+        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, tm[2 * kTP], Z, 0, 0, 0);
+        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, tm[3 * kTP], Z, 0, 0, 0);
+      }
+      // T_{ib,jb} = -T_{ib,ib} Z: Z's accumulator element q is its row 4 g + q
+      const float4 d = *(const float4*)(S + tri(ib, ib) * kTile + i * kTP + 4 * g);
+      f32x4 t = zero4();
+      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.x, Z[0], t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.y, Z[1], t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.z, Z[2], t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.w, Z[3], t, 0, 0, 0);
+      R[jb] = t;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int jb = 0; jb < ib; ++jb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[tri(ib, jb) * kTile + (4 * g + j) * kTP + i] = -R[jb][j];
+    wave_lds_sync();
+  }
 }
 
-template <class Arm, int DK, int C, bool KDA, bool QF32>
-__global__ __launch_bounds__(256) void gdn_prep(Params p) {
-  using T = typename Arm::T;
+// From the lower tiles of the two chunk products, oriented with lanes as rows (element j
+// of tile (rt, st) in lane (i, g) is row r = 16 rt + i, column s = 16 st + 4 g + j):
+//   A = tril_strict(beta_r e^{G_r - G_s} KK),  P = tril(e^{G_r - G_s} QK), rows r < L
+// (per-channel gate: the exponentials are already inside the products, G unused);
+// then T = (I + A)^-1 in this wave's LDS S, and T, P stored as scan fragments.
+template <class Arm, int C, bool KDA>
+__device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, const float* Gs,
+                                           const float* Bs, typename Arm::T* Tout,
+                                           typename Arm::T* Pout, int L, int lane) {
+  constexpr int NT = C / 16;
+  const int i = lane & 15, g = lane >> 4;
+  wave_lds_sync();  // G and beta rows written by other lanes
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const float Gr = KDA ? 0.f : Gs[16 * rt + i];
+    const float br = Bs[16 * rt + i];  // zero for rows past the chunk end
+    const bool live = 16 * rt + i < L;
+#pragma unroll
+    for (int st = 0; st <= rt; ++st) {
+      const int t = tri(rt, st);
+      float4 G4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!KDA) G4 = *(const float4*)(Gs + 16 * st + 4 * g);
+      const float Gsv[4] = {G4.x, G4.y, G4.z, G4.w};
+      f32x4 a, pv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool lower = st < rt || 4 * g + j < i;
+        const bool ldiag = live && (st < rt || 4 * g + j <= i);
+        const float e = KDA ? 1.f : nexp(Gr - Gsv[j]);  // s > r entries are discarded
+        a[j] = lower ? br * (e * accA[t][j]) : 0.f;
+        pv[j] = ldiag ? e * accP[t][j] : 0.f;
+      }
+      *(float4*)(S + t * kTile + i * kTP + 4 * g) = (float4){a[0], a[1], a[2], a[3]};
+      accP[t] = pv;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+    for (int sb = 0; sb <= (mt >> 1); ++sb) {
+      const f32x4 hi = (2 * sb + 1 <= mt) ? accP[tri(mt, (2 * sb + 1 <= mt) ? 2 * sb + 1 : 0)] : zero4();
+      Arm::st8(Pout + (tile_frag_index(mt, sb) * 64 + lane) * 8, accP[tri(mt, 2 * sb)], hi);
+    }
+  wave_lds_sync();
+  wave_solve_unit_lower<C>(S, lane);
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+    for (int sb = 0; sb <= (mt >> 1); ++sb) {
+      const float4 l4 = *(const float4*)(S + tri(mt, 2 * sb) * kTile + i * kTP + 4 * g);
+      float4 h4 = {0.f, 0.f, 0.f, 0.f};
+      if (2 * sb + 1 <= mt) h4 = *(const float4*)(S + tri(mt, 2 * sb + 1) * kTile + i * kTP + 4 * g);
+      Arm::st8(Tout + (tile_frag_index(mt, sb) * 64 + lane) * 8, (f32x4){l4.x, l4.y, l4.z, l4.w},
+               (f32x4){h4.x, h4.y, h4.z, h4.w});
+    }
+}
+
+// A fragment from the raw 16-byte loads of its 8 input elements (bf16: one load, fp32: two).
+template <class Arm, bool QF32>
+__device__ __forceinline__ typename Arm::F frag_of(const u32x4* raw) {
+  if constexpr (QF32) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(raw[j >> 2][j & 3]);
+    return Arm::from_f32(x);
+  } else {
+    return Arm::from_bf16(raw[0]);
+  }
+}
+
+// ----------------------------------------------------------- prep -------
+// Per-head gate: one wave per (chunk slot, value head), four per workgroup, no barrier.
+// The wave takes its K and Q operand fragments straight from global memory (the waves
+// of one key head's value heads are neighbours and share them through the caches),
+// forms KK^T and (Q K^T) lower tiles on MFMA (contraction over dk in contiguous
+// 8-element pieces), runs its gate sweep, and hands the products to wave_tiles.
+template <class Arm, int DK, int C, bool QF32>
+__global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
   using F = typename Arm::F;
-  constexpr int NT = C / 16, NBK = DK / 32, KP = DK + Arm::PAD, AP = C + 4;
-  constexpr int NTRI = NT * (NT + 1) / 2, NTILE = 2 * NTRI, MAXT = (NTILE + 3) / 4;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
-  const int heads = KDA ? p.hv : p.hk;
-  const int head = blockIdx.x % heads;
-  const int64_t slot = blockIdx.x / heads;
+  using SL = SolveLds<C>;
+  constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32;
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
+  const int64_t unit = (int64_t)blockIdx.x * 4 + w;
+  const int64_t slot = unit / p.hv;
+  const int h = (int)(unit - slot * p.hv);
   int n, L;
   int64_t t0;
-  if (!locate_chunk(p, C, slot, n, t0, L)) return;
-  const int group = p.hv / p.hk;
-  const int kh = KDA ? head / group : head;
-
-  T* X0 = (T*)gdn_smem;  // K (scalar gate) or K*e^{G-Gm} (per-channel gate)
-  T* X1 = X0 + C * KP;   // Q                or K*e^{Gm-G}
-  T* X2 = X1 + C * KP;   // --               or Q*e^{G-Gm}
-  T* Y0 = X2 + C * KP;   // per-channel gate, for the scan: e^{G} K, e^{G_C-G} K, e^{G} Q
-  float* Am = (float*)(X0 + (KDA ? 6 : 2) * C * KP);
-  float* Tm = Am + C * AP;
-  T* Pst = (T*)(Tm + C * AP);
-  float* Gs = (float*)(Pst + C * C);
+  if (slot >= p.max_slots || !locate_chunk(p, C, slot, n, t0, L)) return;
+  const int kh = h / (p.hv / p.hk);
+  float* S = (float*)gdn_smem + w * SL::FLOATS;
+  float* Gs = S + NTRI * kTile;
   float* Bs = Gs + C;
   uint32_t bad = 0;
 
-  if constexpr (!KDA) {
-    // every load first (rows past the chunk end re-read the last valid row, in bounds),
-    // then the stores; no branch around a load
-    constexpr int EPC = QF32 ? 4 : 8, ESZ = QF32 ? 4 : 2, NP = C * DK / EPC;
-    constexpr int NL = (NP + 255) / 256;
-    u32x4 ka[NL], qa[NL];
+  // every global load first (gate and beta, then all K and Q fragments), then the math.
+  // Rows past a partial chunk's end re-read its last row (in bounds); their beta is
+  // zero, so their A rows vanish, and P masks them at formation.
+  const int rg = lane < L ? lane : L - 1;
+  const float xl = p.g[(t0 + rg) * p.hv + h], bl = p.beta[(t0 + rg) * p.hv + h];
+  constexpr int ESZ = QF32 ? 4 : 2, EPL = QF32 ? 2 : 1;  // 16-byte loads per fragment
+  const int64_t cbase = (t0 * p.hk + kh) * (int64_t)(DK * ESZ);  // chunk's first row
+  const char* kbase = (const char*)p.k + cbase;
+  const char* qbase = (const char*)p.q + cbase;
+  const uint32_t rstride = (uint32_t)(p.hk * DK * ESZ);
+  u32x4 rk[NBK][NT][EPL], rq[NBK][NT][EPL];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int idx = tid + 256 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
-      const int rr = (r < L ? r : L - 1) % C;  // pieces past NP (tiny widths) re-read row 0..C-1
-      const int64_t off = (((t0 + rr) * p.hk + kh) * (int64_t)DK + c * EPC) * ESZ;
-      ka[j] = ld16(p.k, off);
-      qa[j] = ld16(p.q, off);
-    }
+  for (int rt = 0; rt < NT; ++rt) {
+    const int r = 16 * rt + i;
+    const uint32_t o = (uint32_t)(r < L ? r : L - 1) * rstride + 8 * g * ESZ;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int idx = tid + 256 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
-      if (NP % 256 != 0 && idx >= NP) break;
-      const u32x4 kz = (r < L) ? ka[j] : (u32x4)(0u), qz = (r < L) ? qa[j] : (u32x4)(0u);
-      if (nonfinite16<QF32>(kz) || nonfinite16<QF32>(qz)) bad |= GDN_ST_NONFINITE_INPUT;
-      put16<Arm, QF32>(kz, X0 + r * KP + c * EPC);
-      put16<Arm, QF32>(qz, X1 + r * KP + c * EPC);
-    }
-  } else {
-    // per-channel gate: one thread per key channel walks the chunk rows; factors are
-    // split around the middle row m so every stored factor stays <= e^80 (gate >= -5,
-    // C = 32); exponent arguments are clamped, masked entries removed by select below.
-    const int hv = head;
-    if (tid < DK) {
-      const int d = tid;
-      float G[C];
-      float acc = 0.f;
+    for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
-        const int rr = r < L ? r : L - 1;
-        const float xl = p.g[((t0 + rr) * p.hv + hv) * (int64_t)DK + d];
-        const float x = r < L ? xl : 0.f;
-        if (f_nonfinite(x)) bad |= GDN_ST_NONFINITE_INPUT;
-        else if (x > 0.f || x < -5.f) bad |= GDN_ST_GATE_DOMAIN;
-        acc += x;
-        G[r] = acc;
+      for (int x = 0; x < EPL; ++x) {
+        rk[kb][rt][x] = *(const u32x4*)(kbase + o + (32 * kb + 4 * x) * ESZ);
+        rq[kb][rt][x] = *(const u32x4*)(qbase + o + (32 * kb + 4 * x) * ESZ);
       }
-      const float Gm = G[C / 2];
-      const float GC = G[C - 1];
-      T* Y1 = Y0 + C * KP;
-      T* Y2 = Y1 + C * KP;
-#pragma unroll
-      for (int r = 0; r < C; ++r) {
-        const int rr = r < L ? r : L - 1;
-        const int64_t e = ((t0 + rr) * p.hk + kh) * (int64_t)DK + d;
-        const float kl = load1(p.k, e, QF32), ql = load1(p.q, e, QF32);
-        const float kf = r < L ? kl : 0.f, qf = r < L ? ql : 0.f;
-        if (f_nonfinite(kf) || f_nonfinite(qf)) bad |= GDN_ST_NONFINITE_INPUT;
-        const float up = nexp(fminf(G[r] - Gm, 85.f)), dn = nexp(fminf(Gm - G[r], 85.f));
-        X0[r * KP + d] = Arm::cvt(kf * up);
-        X1[r * KP + d] = Arm::cvt(kf * dn);
-        X2[r * KP + d] = Arm::cvt(qf * up);
-        const float eg = nexp(G[r]);
-        Y0[r * KP + d] = Arm::cvt(eg * kf);
-        Y1[r * KP + d] = Arm::cvt(nexp(GC - G[r]) * kf);
-        Y2[r * KP + d] = Arm::cvt(eg * qf);
-      }
-      p.Dws[(slot * p.hv + hv) * (int64_t)DK + d] = nexp(GC);
+  }
+  {  // gate sweep and beta of row `lane`
+    const float x = lane < L ? xl : 0.f, b = lane < L ? bl : 0.f;
+    bad |= flag_if(f_nonfinite(x) | f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
+    bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
+    const float G = wave_prefix_sum(x, lane);
+    if (lane < C) {
+      Gs[lane] = G;
+      Bs[lane] = b;
     }
+  }
+  if (h % (p.hv / p.hk) == 0) {  // K and Q checked once per key head (wave-uniform)
+    uint32_t nf = 0;
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) nf |= nf_bits16<QF32>(rk[kb][rt][x]) | nf_bits16<QF32>(rq[kb][rt][x]);
+    bad |= flag_if(nf, GDN_ST_NONFINITE_INPUT);
+  }
+
+  f32x4 accA[NTRI], accP[NTRI];
+#pragma unroll
+  for (int t = 0; t < NTRI; ++t) {
+    accA[t] = zero4();
+    accP[t] = zero4();
+  }
+#pragma unroll
+  for (int kb = 0; kb < NBK; ++kb) {
+    F kf[NT], qf[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      kf[rt] = frag_of<Arm, QF32>(rk[kb][rt]);
+      qf[rt] = frag_of<Arm, QF32>(rq[kb][rt]);
+    }
+    // tile (rt, st): A operand = rows of tile st, B operand = rows of tile rt, so the
+    // accumulator's lanes are the rows r of tile rt
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int st = 0; st <= rt; ++st) {
+        accA[tri(rt, st)] = Arm::mma(kf[st], kf[rt], accA[tri(rt, st)]);
+        accP[tri(rt, st)] = Arm::mma(kf[st], qf[rt], accP[tri(rt, st)]);
+      }
+  }
+  typedef typename Arm::T T;
+  const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
+  wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
+  if (bad) atomicOr(p.status, bad);
+}
+
+// Per-channel gate (C = 32): one workgroup per (chunk slot, value head).  One thread per
+// key channel sweeps the gate down the chunk and forms the gated operands: for the
+// products, factors split around the middle row m so every stored factor stays below
+// e^85 (gate >= -5, C = 32; arguments clamped, masked entries dropped by select):
+//   Kup = K e^{G - G_m},  Kdn = K e^{G_m - G},  Qup = Q e^{G - G_m}   (LDS)
+// and for the scan e^{G} K, e^{G_C - G} K, e^{G} Q and e^{G_C} (workspace).  Then wave 0
+// forms Kup Kdn^T and Qup Kdn^T on MFMA and hands them to wave_tiles.
+template <class Arm, int DK>
+constexpr size_t prep_chan_lds_bytes() {
+  return 3 * (size_t)32 * (DK + Arm::PAD) * sizeof(typename Arm::T) + SolveLds<32>::FLOATS * sizeof(float);
+}
+
+template <class Arm, int DK, bool QF32>
+__global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
+  using T = typename Arm::T;
+  using F = typename Arm::F;
+  constexpr int C = 32, NT = 2, NBK = DK / 32, KP = DK + Arm::PAD;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int h = (int)(blockIdx.x % p.hv);
+  const int64_t slot = blockIdx.x / p.hv;
+  int n, L;
+  int64_t t0;
+  if (!locate_chunk(p, C, slot, n, t0, L)) return;  // uniform over the workgroup
+  const int kh = h / (p.hv / p.hk);
+  T* Kup = (T*)gdn_smem;
+  T* Kdn = Kup + C * KP;
+  T* Qup = Kdn + C * KP;
+  float* S = (float*)(Qup + C * KP);
+  float* Gs = S + SolveLds<C>::NTRI * kTile;
+  float* Bs = Gs + C;
+  uint32_t bad = 0;
+
+  if (tid < DK) {
+    const int d = tid;
+    float G[C];
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const int rr = r < L ? r : L - 1;
+      const float xl = p.g[((t0 + rr) * p.hv + h) * (int64_t)DK + d];
+      const float x = r < L ? xl : 0.f;
+      bad |= flag_if(f_nonfinite(x), GDN_ST_NONFINITE_INPUT);
+      bad |= flag_if((x > 0.f) | (x < -5.f), GDN_ST_GATE_DOMAIN);
+      acc += x;
+      G[r] = acc;
+    }
+    const float Gm = G[C / 2];
+    const float GC = G[C - 1];
+    T* Y = (T*)p.Gws + (slot * p.hv + h) * (int64_t)(3 * C * DK) + d;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const int rr = r < L ? r : L - 1;
+      const int64_t e = ((t0 + rr) * p.hk + kh) * (int64_t)DK + d;
+      const float kl = load1(p.k, e, QF32), ql = load1(p.q, e, QF32);
+      const float kf = r < L ? kl : 0.f, qf = r < L ? ql : 0.f;
+      bad |= flag_if(f_nonfinite(kf) | f_nonfinite(qf), GDN_ST_NONFINITE_INPUT);
+      const float up = nexp(fminf(G[r] - Gm, 85.f)), dn = nexp(fminf(Gm - G[r], 85.f));
+      Kup[r * KP + d] = Arm::cvt(kf * up);
+      Kdn[r * KP + d] = Arm::cvt(kf * dn);
+      Qup[r * KP + d] = Arm::cvt(qf * up);
+      const float eg = nexp(G[r]);
+      Y[(0 * C + r) * DK] = Arm::cvt(eg * kf);
+      Y[(1 * C + r) * DK] = Arm::cvt(nexp(GC - G[r]) * kf);
+      Y[(2 * C + r) * DK] = Arm::cvt(eg * qf);
+    }
+    p.Dws[(slot * p.hv + h) * (int64_t)DK + d] = nexp(GC);
   }
   __syncthreads();
-  if constexpr (KDA) {
-    constexpr int EPT = 16 / (int)sizeof(T);
-    T* Gg = (T*)p.Gws + (slot * p.hv + head) * (int64_t)(3 * C * DK);
-    for (int idx = tid; idx < 3 * C * DK / EPT; idx += 256) {
-      const int e0 = idx * EPT, m = e0 / (C * DK), r = (e0 / DK) % C, c = e0 % DK;
-      *(uint4*)(Gg + e0) = *(const uint4*)(Y0 + (m * C + r) * KP + c);
+  if (w == 0) {
+    {
+      const int rr = lane < L ? lane : L - 1;
+      const float bl = p.beta[(t0 + rr) * p.hv + h];
+      const float b = lane < L ? bl : 0.f;
+      bad |= flag_if(f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
+      if (lane < C) Bs[lane] = b;
     }
-  }
-
-  // Products on MFMA: tile list = lower tiles (rt >= st) of the two C x C products.
-  // scalar gate: KK^T and QK^T;  per-channel gate: Kup Kdn^T and Qup Kdn^T.
-  f32x4 acc[MAXT];
+    f32x4 accA[3], accP[3];
 #pragma unroll
-  for (int j = 0; j < MAXT; ++j) {
-    acc[j] = zero4();
-    const int tix = w + 4 * j;
-    if (tix < NTILE) {
-      const int which = tix / NTRI;
-      int t = tix % NTRI, rt = 0;
-      while (t > rt) { t -= rt + 1; ++rt; }
-      const int st = t;
-      const T* Am_ = which ? (KDA ? X2 : X1) : X0;
-      const T* Bm_ = KDA ? X1 : X0;
-      const T* arow = Am_ + (16 * rt + i) * KP;
-      const T* brow = Bm_ + (16 * st + i) * KP;
+    for (int t = 0; t < 3; ++t) {
+      accA[t] = zero4();
+      accP[t] = zero4();
+    }
 #pragma unroll
-      for (int kb = 0; kb < NBK; ++kb) {
-        F a = Arm::row(arow + 32 * kb + 4 * g, arow + 32 * kb + 16 + 4 * g);
-        F b = Arm::row(brow + 32 * kb + 4 * g, brow + 32 * kb + 16 + 4 * g);
-        acc[j] = Arm::mma(a, b, acc[j]);
+    for (int kb = 0; kb < NBK; ++kb) {
+      F up[NT], dn[NT], qu[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        const int o = (16 * rt + i) * KP + 32 * kb + 8 * g;
+        up[rt] = Arm::ld8(Kup + o);
+        dn[rt] = Arm::ld8(Kdn + o);
+        qu[rt] = Arm::ld8(Qup + o);
       }
-    }
-  }
-
-  const int nheads = KDA ? 1 : group;
-  for (int jh = 0; jh < nheads; ++jh) {
-    const int hv = KDA ? head : kh * group + jh;
-    if (w == 0) {
-      const int r = lane;
-      float x = 0.f, b = 0.f;
-      if (r < L) {
-        const int64_t e = (t0 + r) * p.hv + hv;
-        b = p.beta[e];
-        if (f_nonfinite(b)) bad |= GDN_ST_NONFINITE_INPUT;
-        if constexpr (!KDA) {
-          x = p.g[e];
-          if (f_nonfinite(x)) bad |= GDN_ST_NONFINITE_INPUT;
-          else if (x > 0.f) bad |= GDN_ST_GATE_DOMAIN;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int st = 0; st <= rt; ++st) {
+          accA[tri(rt, st)] = Arm::mma(dn[st], up[rt], accA[tri(rt, st)]);
+          accP[tri(rt, st)] = Arm::mma(dn[st], qu[rt], accP[tri(rt, st)]);
         }
-      }
-      const float G = wave_prefix_sum(x, lane);
-      if (r < C) {
-        Gs[r] = G;
-        Bs[r] = b;
-      }
     }
-    __syncthreads();
-    // A (strictly lower, beta-scaled) and P (lower with diagonal) from the accumulators
-#pragma unroll
-    for (int j = 0; j < MAXT; ++j) {
-      const int tix = w + 4 * j;
-      if (tix < NTILE) {
-        const int which = tix / NTRI;
-        int t = tix % NTRI, rt = 0;
-        while (t > rt) { t -= rt + 1; ++rt; }
-        const int st = t;
-        const int s = 16 * st + i;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int r = 16 * rt + 4 * g + ii;
-          float val;
-          if constexpr (KDA) {
-            val = acc[j][ii];
-          } else {
-            val = (s <= r) ? nexp(Gs[r] - Gs[s]) * acc[j][ii] : 0.f;
-          }
-          if (which == 0)
-            Am[r * AP + s] = (s < r) ? Bs[r] * val : 0.f;
-          else
-            Pst[r * C + s] = Arm::cvt((s <= r) ? val : 0.f);
-        }
-      }
-    }
-    for (int idx = tid; idx < C * C; idx += 256) {  // tiles above the diagonal
-      const int r = idx / C, s = idx % C;
-      if ((s >> 4) > (r >> 4)) {
-        Am[r * AP + s] = 0.f;
-        Pst[r * C + s] = Arm::cvt(0.f);
-      }
-    }
-    __syncthreads();
-    T* Pg = (T*)p.Pws + (slot * p.hv + hv) * (int64_t)(C * C);
-    for (int idx = tid; idx < C * C / 8; idx += 256) copy8<Arm>(Pst + 8 * idx, Pg + 8 * idx);
-    solve_unit_lower<C>(Am, Tm, tid);
-    T* Tg = (T*)p.Tws + (slot * p.hv + hv) * (int64_t)(C * C);
-    constexpr int EPT = 16 / (int)sizeof(T);
-    for (int idx = tid; idx < C * C / EPT; idx += 256) {
-      const int e0 = idx * EPT, r = e0 / C, c = e0 % C;
-      const float* src = Tm + r * AP + c;
-      if constexpr (sizeof(T) == 2) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f2bf(src[2 * j]) | ((uint32_t)f2bf(src[2 * j + 1]) << 16);
-        *(u32x4*)(Tg + e0) = w;
-      } else {
-        *(float4*)(Tg + e0) = *(const float4*)src;
-      }
-    }
-    __syncthreads();
+    const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
+    wave_tiles<Arm, C, true>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
   }
   if (bad) atomicOr(p.status, bad);
 }
@@ -683,7 +735,7 @@ struct ScanStageDims {
   using T = typename Arm::T;
   static constexpr int EPC = QF32 ? 4 : 8;                           // input elements per 16 bytes
   static constexpr int NKQ = C * DK / EPC / 128;                     // K (and Q) rows
-  static constexpr int NTP = C * C * (int)sizeof(T) / 16 / 128;      // T (and P)
+  static constexpr int NTP = tile_elems(C) * (int)sizeof(T) / 16 / 128;  // T (and P) fragments
   static constexpr int NV = C * 32 / EPC / 128;                      // the 32 V columns
   static constexpr int NG = 3 * C * DK * (int)sizeof(T) / 16 / 128;  // gated operands
 };
@@ -692,7 +744,7 @@ struct ScanStageDims {
 template <class Arm, int DK, int C>
 constexpr size_t scan_buf_bytes(bool kda) {
   return (size_t)(kda ? 3 : 2) * C * (DK + Arm::PAD) * sizeof(typename Arm::T)  // K [, K~], Q
-         + 2 * (size_t)C * (C + Arm::PAD) * sizeof(typename Arm::T)            // T, P
+         + 2 * (size_t)tile_elems(C) * sizeof(typename Arm::T)                 // T, P fragments
          + (size_t)C * 36 * sizeof(float)                                      // V (32 columns)
          + (4 * (size_t)C + DK + 4) * sizeof(float);                           // row scalars
 }
@@ -718,7 +770,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
   using F = typename Arm::F;
   using Stage = ScanStageDims<Arm, DK, C, KDA, QF32>;
   constexpr int NT = C / 16, NBC = C / 32, NTK = DK / 16, NBK = DK / 32;
-  constexpr int KP = DK + Arm::PAD, CP = C + Arm::PAD, VP = 36;
+  constexpr int KP = DK + Arm::PAD, VP = 36;
   constexpr int EPC = Stage::EPC, ESZ = QF32 ? 4 : 2;
   constexpr int EPT = 16 / (int)sizeof(T);  // arm elements per 16 bytes
   constexpr int NBUF = scan_nbuf<Arm, DK, C>(KDA);
@@ -755,8 +807,8 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
     B.Kl = KDA ? B.Ks + C * KP : B.Ks;    // per channel: e^{G_C - G} K
     B.Qs = B.Ks + (KDA ? 2 : 1) * C * KP; // Q or e^{G} Q
     B.Ts = B.Qs + C * KP;
-    B.Ps = B.Ts + C * CP;
-    B.Vs = (float*)(B.Ps + C * CP);
+    B.Ps = B.Ts + tile_elems(C);
+    B.Vs = (float*)(B.Ps + tile_elems(C));
     B.sb_ = B.Vs + C * VP;  // beta
     B.sbe = B.sb_ + C;      // beta e^{G}
     B.seg = B.sbe + C;      // e^{G}
@@ -838,8 +890,8 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       for (int j = 0; j < Stage::NG; ++j) skg[rs][j] = Gg[ltid + 128 * j];
       if (ltid < DK) sdc[rs] = p.Dws[(slot * p.hv + h) * (int64_t)DK + ltid];
     }
-    const u32x4* Tg = (const u32x4*)((const T*)p.Tws + (slot * p.hv + h) * (int64_t)(C * C));
-    const u32x4* Pg = (const u32x4*)((const T*)p.Pws + (slot * p.hv + h) * (int64_t)(C * C));
+    const u32x4* Tg = (const u32x4*)((const T*)p.Tws + (slot * p.hv + h) * (int64_t)tile_elems(C));
+    const u32x4* Pg = (const u32x4*)((const T*)p.Pws + (slot * p.hv + h) * (int64_t)tile_elems(C));
 #pragma unroll
     for (int j = 0; j < Stage::NTP; ++j) {
       stt[rs][j] = Tg[ltid + 128 * j];
@@ -891,15 +943,14 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < Stage::NTP; ++j) {
-      const int e0 = (ltid + 128 * j) * EPT, r = e0 / C, c = e0 % C;
-      *(u32x4*)(B.Ts + r * CP + c) = stt[rs][j];
-      *(u32x4*)(B.Ps + r * CP + c) = spp[rs][j];
+    for (int j = 0; j < Stage::NTP; ++j) {  // fragments, verbatim
+      *(u32x4*)(B.Ts + (ltid + 128 * j) * EPT) = stt[rs][j];
+      *(u32x4*)(B.Ps + (ltid + 128 * j) * EPT) = spp[rs][j];
     }
 #pragma unroll
     for (int j = 0; j < Stage::NV; ++j) {
       const int idx = ltid + 128 * j, r = idx / (32 / EPC), c = idx % (32 / EPC);
-      if (nonfinite16<QF32>(sv[rs][j])) bad |= GDN_ST_NONFINITE_INPUT;
+      bad |= flag_if(nonfinite16<QF32>(sv[rs][j]), GDN_ST_NONFINITE_INPUT);
       put16f<QF32>(sv[rs][j], B.Vs + r * VP + c * EPC);
     }
   };
@@ -952,10 +1003,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
     for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
-        if (32 * sb <= 16 * mt + 15) {
-          const T* trow = B.Ts + (16 * mt + i) * CP + 32 * sb + 4 * g;
-          tf[sb][mt] = Arm::row(trow, trow + 16);
-        }
+        if (32 * sb <= 16 * mt + 15) tf[sb][mt] = Arm::ld8(B.Ts + (tile_frag_index(mt, sb) * 64 + lane) * 8);
     f32x4 O[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) O[nt] = zero4();
@@ -1001,10 +1049,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
     for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        if (32 * sb <= 16 * nt + 15) {
-          const T* prow = B.Ps + (16 * nt + i) * CP + 32 * sb + 4 * g;
-          pf[sb][nt] = Arm::row(prow, prow + 16);
-        }
+        if (32 * sb <= 16 * nt + 15) pf[sb][nt] = Arm::ld8(B.Ps + (tile_frag_index(nt, sb) * 64 + lane) * 8);
     __builtin_amdgcn_sched_barrier(0);
 
     F RO[NBC], RS[NBC];
@@ -1053,8 +1098,8 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       const int r = 16 * nt + i;
       if (r < L) {
         const f32x4 o = O[nt];
-        if (f_nonfinite(o[0]) || f_nonfinite(o[1]) || f_nonfinite(o[2]) || f_nonfinite(o[3]))
-          bad |= GDN_ST_NONFINITE_OUTPUT;
+        bad |= flag_if(f_nonfinite(o[0]) | f_nonfinite(o[1]) | f_nonfinite(o[2]) | f_nonfinite(o[3]),
+                       GDN_ST_NONFINITE_OUTPUT);
         const int64_t e = ((t0 + r) * p.hv + h) * (int64_t)DV + col0 + 4 * g;
         if (p.o_f32) {
           *(float4*)((float*)p.o + e) = (float4){o[0], o[1], o[2], o[3]};
@@ -1116,7 +1161,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       for (int t = 0; t < NTK; ++t)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          if (f_nonfinite(H[t][ii])) bad |= GDN_ST_NONFINITE_INPUT;
+          bad |= flag_if(f_nonfinite(H[t][ii]), GDN_ST_NONFINITE_INPUT);
     } else {
 #pragma unroll
       for (int t = 0; t < NTK; ++t) H[t] = zero4();
@@ -1139,7 +1184,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int d = 16 * t + 4 * g + ii;
-          if (f_nonfinite(H[t][ii])) bad |= GDN_ST_NONFINITE_OUTPUT;
+          bad |= flag_if(f_nonfinite(H[t][ii]), GDN_ST_NONFINITE_OUTPUT);
           p.hT[hbase + (int64_t)d * DV + col0 + i] = H[t][ii];
         }
       }
@@ -1166,10 +1211,17 @@ bool set_lds_once(Fn fn, size_t lds) {
 template <class Arm, int DK, int C, bool KDA, bool QF32>
 gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
   if (pl.run_prep && pl.max_slots > 0) {
-    const size_t lds = prep_lds_bytes<Arm, DK, C>(KDA);
-    if (!set_lds_once(gdn_prep<Arm, DK, C, KDA, QF32>, lds)) return GDN_E_LAUNCH;
-    const int64_t blocks = pl.max_slots * (KDA ? pl.hv : pl.hk);
-    hipLaunchKernelGGL((gdn_prep<Arm, DK, C, KDA, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+    if constexpr (KDA) {
+      const size_t lds = prep_chan_lds_bytes<Arm, DK>();
+      if (!set_lds_once(gdn_prep_chan<Arm, DK, QF32>, lds)) return GDN_E_LAUNCH;
+      const int64_t blocks = pl.max_slots * pl.hv;
+      hipLaunchKernelGGL((gdn_prep_chan<Arm, DK, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+    } else {
+      const size_t lds = 4 * SolveLds<C>::FLOATS * sizeof(float);
+      if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, lds)) return GDN_E_LAUNCH;
+      const int64_t blocks = (pl.max_slots * pl.hv + 3) / 4;
+      hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+    }
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   if (pl.run_scan) {

@@ -96,18 +96,40 @@ def oracle_units(inp, units, want_o=True):
     return out
 
 
+def tile_frags(C):
+    """(mt, sb) of the stored fragments of a C x C lower-triangular tile, in order."""
+    return [(mt, sb) for mt in range(C // 16) for sb in range(mt // 2 + 1)]
+
+
+def decode_tiles(frag, C):
+    """Dense [..., C, C] tiles from stored fragments [..., n_frag, 64, 8]: fragment (mt, sb),
+    lane l = 16 g + i, element e holds row 16 mt + i, column 32 sb + 4 g + e (e < 4) or
+    32 sb + 16 + 4 g + e - 4 (e >= 4); entries no fragment covers are zero."""
+    import torch
+    out = torch.zeros(frag.shape[:-3] + (C, C), dtype=frag.dtype, device=frag.device)
+    lane = torch.arange(64)
+    i, g = lane % 16, lane // 16
+    for f, (mt, sb) in enumerate(tile_frags(C)):
+        for e in range(8):
+            col = 32 * sb + 4 * g + (e if e < 4 else 16 + e - 4)
+            out[..., 16 * mt + i, col] = frag[..., f, :, e]
+    return out
+
+
 def workspace_tile_views(prob, ws, arm_f32):
-    """T and P tiles inside the library's workspace for a fixed-length problem
-    (layout: T tiles [slot][hv][C][C], then P tiles, each region 256-byte aligned)."""
+    """T and P tiles inside the library's workspace for a fixed-length problem, decoded to
+    dense [slot][hv][C][C] (layout: T fragments [slot][hv][n_frag][64][8], then P
+    fragments, each region 256-byte aligned)."""
     import torch
     C = prob.chunk
     esz = 4 if arm_f32 else 2
+    nf = len(tile_frags(C))
     cps = (prob.seq_len + C - 1) // C
     slots = prob.n_seq * cps
-    n = slots * prob.hv * C * C
+    n = slots * prob.hv * nf * 512
     tile_bytes = n * esz
     off_p = (tile_bytes + 255) // 256 * 256
     dt = torch.float32 if arm_f32 else torch.bfloat16
-    T = ws[:tile_bytes].view(dt).view(slots, prob.hv, C, C)
-    P = ws[off_p:off_p + tile_bytes].view(dt).view(slots, prob.hv, C, C)
-    return T, P
+    T = ws[:tile_bytes].view(dt).view(slots, prob.hv, nf, 64, 8)
+    P = ws[off_p:off_p + tile_bytes].view(dt).view(slots, prob.hv, nf, 64, 8)
+    return decode_tiles(T, C), decode_tiles(P, C)

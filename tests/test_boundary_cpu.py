@@ -78,15 +78,19 @@ def test_validate_null_problem():
 
 
 def test_workspace_bytes_scales_with_tiles():
-    # per chunk slot and value head: T and P, C x C each, bf16 (2 B) or fp32 (4 B)
-    b16 = gdn.workspace_bytes(P(chunk=64))
-    f32 = gdn.workspace_bytes(P(chunk=64, arm=gdn.ARM_FOLD_F32))
-    slots, hv, C = 4, 6, 64
-    assert b16 >= 2 * slots * hv * C * C * 2 and b16 < 2 * slots * hv * C * C * 2 + 1024
-    assert f32 >= 2 * slots * hv * C * C * 4
+    # per chunk slot and value head: T and P, each stored as the lower-triangle MFMA
+    # fragments of a C x C tile (C = 64: 6 of the 8 fragments of 16 x 32, 3072 elements;
+    # C = 32: 2 fragments, 1024), bf16 (2 B) or fp32 (4 B)
+    slots, hv = 4, 6
+    for C, elems in ((64, 3072), (32, 1024)):
+        b16 = gdn.workspace_bytes(P(chunk=C))
+        f32 = gdn.workspace_bytes(P(chunk=C, arm=gdn.ARM_FOLD_F32))
+        s = slots * 64 // C
+        assert 2 * s * hv * elems * 2 <= b16 < 2 * s * hv * elems * 2 + 1024
+        assert 2 * s * hv * elems * 4 <= f32 < 2 * s * hv * elems * 4 + 1024
     # packed form: slots bounded by ceil(total / C) + n_seq, plus the chunk table
     pk = gdn.workspace_bytes(P(n_seq=3, seq_len=0, chunk=64))
-    assert pk >= 2 * (4 + 3) * hv * C * C * 2
+    assert pk >= 2 * (4 + 3) * hv * 3072 * 2
 
 
 # fake, well-aligned device addresses: the host checks below return before any launch
