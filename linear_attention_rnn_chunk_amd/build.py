@@ -13,6 +13,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 ALU forms are kept out of every code object
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core results in ordinary VGPRs: the recurrence scales and converts its
+         # accumulators with vector ALU ops, which cannot address AGPRs directly
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 

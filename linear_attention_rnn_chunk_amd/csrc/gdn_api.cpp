@@ -82,6 +82,14 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   off = round_up(off + gated, 256);
   pl.off_D = off;
   off = round_up(off + decb, 256);
+  // per-head gate with fp32 inputs or the fp32 arm: K and Q in the arm's element type,
+  // written by the sequence-parallel stage so the scan copies them without converting
+  pl.kq_ws = !pl.gate_channel && (pl.qkv_f32 || pl.arm_f32);
+  const size_t kq = pl.kq_ws ? (size_t)pl.max_slots * pl.hk * C * pl.dk * esz : 0;
+  pl.off_K = off;
+  off = round_up(off + kq, 256);
+  pl.off_Q = off;
+  off = round_up(off + kq, 256);
   pl.bytes = off;
   *out = pl;
   return GDN_OK;
@@ -171,6 +179,9 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   prm.Pws = ws ? ws + pl.off_P : nullptr;
   prm.Gws = (ws && pl.gate_channel) ? ws + pl.off_G : nullptr;
   prm.Dws = (ws && pl.gate_channel) ? (float*)(ws + pl.off_D) : nullptr;
+  prm.Kws = (ws && pl.kq_ws) ? ws + pl.off_K : nullptr;
+  prm.Qws = (ws && pl.kq_ws) ? ws + pl.off_Q : nullptr;
+  prm.kq_ws = pl.kq_ws;
   prm.total = pl.total;
   prm.n_seq = pl.n_seq;
   prm.seq_len = pl.seq_len;

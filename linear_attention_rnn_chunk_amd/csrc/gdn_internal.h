@@ -33,7 +33,8 @@ struct Plan {
   int32_t chunks_per_seq;  // fixed-length batches
   int64_t max_slots;     // chunk slots the prep grid covers
   // workspace carve-up (byte offsets)
-  size_t off_table, off_T, off_P, off_G, off_D, bytes;
+  int32_t kq_ws;         // 1: K and Q copied to the workspace in the arm's type
+  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, bytes;
 };
 
 // Kernel arguments (by value).
@@ -53,9 +54,11 @@ struct Params {
   void* Pws;       // [slot][hv][tile_elems(C)] masked P fragments (arm element type)
   void* Gws;       // per-channel gate: [slot][hv][3][C][dk] e^{G} K, e^{G_C-G} K, e^{G} Q
   float* Dws;      // per-channel gate: [slot][hv][dk] e^{G_C}
+  void* Kws;       // kq_ws: [slot][hk][C][dk] K in the arm's element type
+  void* Qws;       // kq_ws: [slot][hk][C][dk] Q in the arm's element type
   int64_t total;
   int32_t n_seq, seq_len, hk, hv, dv;
-  int32_t qkv_f32, o_f32, varlen, chunks_per_seq;
+  int32_t qkv_f32, o_f32, varlen, chunks_per_seq, kq_ws;
   int64_t max_slots;
 };
 

@@ -86,12 +86,42 @@ __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? 
 
 __device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
 
+// four fp32 values as four consecutive bf16 (round to nearest even)
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
+  bf16x4_t b;
+  b[0] = (__bf16)v[0];
+  b[1] = (__bf16)v[1];
+  b[2] = (__bf16)v[2];
+  b[3] = (__bf16)v[3];
+  return __builtin_bit_cast(uint2, b);
+}
+
 __device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP lane moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's (row 2's) last lane is
+// added to row 1 (row 3), then lane 31 to rows 2 and 3.  Lanes a move has no source for
+// add 0 (bound_ctrl), rows outside a move's row mask keep adding 0.
+__device__ __forceinline__ float wave_prefix_sum_dpp(float x) {
+  auto mv = [](float v, auto CTRL, auto ROWS) __attribute__((always_inline)) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(CTRL)::value,
+                                                      decltype(ROWS)::value, 0xf, true));
+  };
+  using std::integral_constant;
+  x += mv(x, integral_constant<int, 0x111>{}, integral_constant<int, 0xf>{});  // row_shr:1
+  x += mv(x, integral_constant<int, 0x112>{}, integral_constant<int, 0xf>{});  // row_shr:2
+  x += mv(x, integral_constant<int, 0x114>{}, integral_constant<int, 0xf>{});  // row_shr:4
+  x += mv(x, integral_constant<int, 0x118>{}, integral_constant<int, 0xf>{});  // row_shr:8
+  x += mv(x, integral_constant<int, 0x142>{}, integral_constant<int, 0xa>{});  // row_bcast:15
+  x += mv(x, integral_constant<int, 0x143>{}, integral_constant<int, 0xc>{});  // row_bcast:31
   return x;
 }
 
@@ -150,6 +180,7 @@ struct ArmBF16 {
   __device__ static __forceinline__ F ld8(const T* p) { return *(const F*)p; }
   // 8 fp32 values (lo then hi) stored as 8 consecutive elements
   __device__ static __forceinline__ void st8(T* p, f32x4 lo, f32x4 hi) { *(F*)p = acc(lo, hi); }
+  __device__ static __forceinline__ void stf(T* p, const F& f) { *(F*)p = f; }
 };
 
 // fp32 MFMA operands (v_mfma_f32_16x16x4_f32, eight per K = 32 fragment).
@@ -214,6 +245,10 @@ struct ArmF32 {
   __device__ static __forceinline__ void st8(T* p, f32x4 lo, f32x4 hi) {
     *(float4*)p = (float4){lo[0], lo[1], lo[2], lo[3]};
     *(float4*)(p + 4) = (float4){hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static __forceinline__ void stf(T* p, const F& f) {
+    *(float4*)p = (float4){f.v[0], f.v[1], f.v[2], f.v[3]};
+    *(float4*)(p + 4) = (float4){f.v[4], f.v[5], f.v[6], f.v[7]};
   }
 };
 
@@ -581,7 +616,7 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
       Bs[lane] = b;
     }
   }
-  if (h % (p.hv / p.hk) == 0) {  // K and Q checked once per key head (wave-uniform)
+  if (h % (p.hv / p.hk) == 0) {  // once per key head (wave-uniform)
     uint32_t nf = 0;
 #pragma unroll
     for (int kb = 0; kb < NBK; ++kb)
@@ -590,6 +625,21 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
 #pragma unroll
         for (int x = 0; x < EPL; ++x) nf |= nf_bits16<QF32>(rk[kb][rt][x]) | nf_bits16<QF32>(rq[kb][rt][x]);
     bad |= flag_if(nf, GDN_ST_NONFINITE_INPUT);
+    if (p.kq_ws) {
+      // K and Q in the arm's element type, [slot][key head][C][DK], for the scan (inputs
+      // in fp32, or the fp32 arm); rows past the chunk end repeat its last row
+      typedef typename Arm::T T;
+      T* kc = (T*)p.Kws + (slot * p.hk + kh) * (int64_t)(C * DK);
+      T* qc = (T*)p.Qws + (slot * p.hk + kh) * (int64_t)(C * DK);
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int o = (16 * rt + i) * DK + 32 * kb + 8 * g;
+          Arm::stf(kc + o, frag_of<Arm, QF32>(rk[kb][rt]));
+          Arm::stf(qc + o, frag_of<Arm, QF32>(rq[kb][rt]));
+        }
+    }
   }
 
   f32x4 accA[NTRI], accP[NTRI];
@@ -729,61 +779,160 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
 }
 
 // ----------------------------------------------------------- scan -------
-// Sizes of the loaders' staging in 16-byte pieces per loader thread (128 of them).
-template <class Arm, int DK, int C, bool KDA, bool QF32>
-struct ScanStageDims {
-  using T = typename Arm::T;
-  static constexpr int EPC = QF32 ? 4 : 8;                           // input elements per 16 bytes
-  static constexpr int NKQ = C * DK / EPC / 128;                     // K (and Q) rows
-  static constexpr int NTP = tile_elems(C) * (int)sizeof(T) / 16 / 128;  // T (and P) fragments
-  static constexpr int NV = C * 32 / EPC / 128;                      // the 32 V columns
-  static constexpr int NG = 3 * C * DK * (int)sizeof(T) / 16 / 128;  // gated operands
+// Serial part: one workgroup per (sequence, value head, 32 state columns), 4 waves:
+//   waves 0, 1  chain: each owns 16 state columns; runs only the recurrence
+//               Y = K H, X = beta V - beta e^G Y, R = T X, H <- e^{G_C} H + Ktil^T R
+//               with its fp32 state in MFMA accumulators
+//   wave 2      output, one chunk behind the chain: O = e^G (Q H_in) + P R for all 32
+//               columns, from H_in and R the chain waves leave in LDS; takes its Q and P
+//               operand fragments straight from global memory into registers
+//   wave 3      loader: copies K, T and V of chunk ci + NBUF - 1 global -> LDS directly
+//               (no register round trip) into a ring of NBUF chunk buffers, runs the
+//               in-chunk gate sweep one chunk ahead, checks V
+// One workgroup barrier per chunk.
+//
+// State rows are stored permuted within each 32-key block: accumulator tile t = 2 kb + h,
+// row 4 g + j holds key dim pi = 32 kb + 8 g + 4 h + j.  Two stacked accumulator tiles are
+// then an MFMA operand fragment whose lane group g covers the 8 contiguous key dims
+// 32 kb + 8 g .. + 7, so the K and Q row fragments are single 16-byte pieces of their rows.
+__device__ __forceinline__ int state_dim(int t, int g, int j) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j; }
+
+// LDS layout of a C x DK operand matrix in row fragments: fragment (mt, kb) holds rows
+// 16 mt .. +15, key columns 32 kb .. +31; its lane slot (i, g) holds row 16 mt + i,
+// columns 32 kb + 8 g .. +7 (16 bytes bf16, 32 fp32).  Slot (i, g) sits at position
+// 4 i + (g ^ ((i >> 1) & 3)): a copy instruction's lanes 4i .. 4i+3 then read one 64-byte
+// piece of row i (coalesced), and the 8 lanes a 16-byte LDS read serves at once land on
+// 8 distinct bank groups.
+template <class Arm, int DK>
+struct OpLayout {
+  typedef typename Arm::T T;
+  static constexpr int NBK = DK / 32;
+  static constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  static constexpr int PPS = 8 / EPP;              // pieces per lane slot
+  template <int C>
+  static constexpr int bytes() { return C * DK * (int)sizeof(T); }
+  __device__ static __forceinline__ int slot_of(int i, int g) { return 4 * i + (g ^ ((i >> 1) & 3)); }
+  // byte offset of element (r, c)
+  __device__ static __forceinline__ int off(int r, int c) {
+    const int kb = c >> 5, g = (c >> 3) & 3, e = c & 7;
+    return (((((r >> 4) * NBK + kb) * 64 + slot_of(r & 15, g)) * PPS + e / EPP) * EPP + e % EPP) *
+           (int)sizeof(T);
+  }
+  // (row, first column) of the elements the 16-byte piece number `pc` holds
+  __device__ static __forceinline__ void piece_src(int pc, int& r, int& c) {
+    const int x = pc % PPS, s = (pc / PPS) & 63, f = pc / (PPS * 64);
+    const int i = s >> 2, g = (s & 3) ^ ((i >> 1) & 3);
+    r = 16 * (f / NBK) + i;
+    c = 32 * (f % NBK) + 8 * g + x * EPP;
+  }
 };
 
-// LDS of one chunk buffer of the scan: operands, T, P, V (fp32), row scalars.
-template <class Arm, int DK, int C>
-constexpr size_t scan_buf_bytes(bool kda) {
-  return (size_t)(kda ? 3 : 2) * C * (DK + Arm::PAD) * sizeof(typename Arm::T)  // K [, K~], Q
-         + 2 * (size_t)tile_elems(C) * sizeof(typename Arm::T)                 // T, P fragments
-         + (size_t)C * 36 * sizeof(float)                                      // V (32 columns)
-         + (4 * (size_t)C + DK + 4) * sizeof(float);                           // row scalars
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global -> LDS without registers: one instruction moves 64 pieces (16 or 4 bytes), lane
+// l's piece to dst + 16 l (dst + 4 l).
+__device__ __forceinline__ void dma16(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
-// Two chunk buffers (the next chunk is written while the current one is read) when they
-// fit in the 160 KiB of LDS, else one.
-template <class Arm, int DK, int C>
-constexpr int scan_nbuf(bool kda) { return 2 * scan_buf_bytes<Arm, DK, C>(kda) <= 150 * 1024 ? 2 : 1; }
-template <class Arm, int DK, int C>
-constexpr size_t scan_lds_bytes(bool kda) {
-  return scan_nbuf<Arm, DK, C>(kda) * ((scan_buf_bytes<Arm, DK, C>(kda) + 255) / 256 * 256);
+__device__ __forceinline__ void dma4(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
 }
 
-// Scan workgroup: 4 waves for 32 state columns of one (sequence, value head).
-//   waves 0, 1  compute: each owns 16 state columns; its fp32 state stays in MFMA
-//               accumulators and only its matrix products run on its SIMD
-//   waves 2, 3  loaders: bring chunk operands from global memory through registers into
-//               the LDS chunk buffers, two chunks ahead (two register sets), and run the
-//               in-chunk gate sweep
-// One barrier per chunk hands a filled buffer from the loaders to the compute waves.
+// s_waitcnt on outstanding vector memory operations only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt at their maximum, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The operand fragment of Op^T for the state update of tile t: rows = state rows of t
+// (key dims state_dim), contraction over the 32 tokens of block sb, token positions
+// {4g..4g+3} then {16+4g..16+4g+3} (the R accumulator layout).
+template <class Arm, int DK>
+__device__ __forceinline__ typename Arm::F kt_frag(const unsigned char* K, int sb, int t, int lane) {
+  typedef OpLayout<Arm, DK> Lay;
+  const int g = lane >> 4, l = lane & 15;
+  const int kb = t >> 1, h = t & 1;
+  if constexpr (sizeof(typename Arm::T) == 2) {
+    // ds_read_b64_tr_b16: within 16 lanes, lane l receives element l%4 of the 8-byte rows
+    // addressed by lanes l/4 + {0, 4, 8, 12}; lane l addresses token 4g + l/4 of the
+    // half-block, key dims 32 kb + 8 (l%4) + 4 h .. +3.
+    const int s0 = 32 * sb + 4 * g + (l >> 2);
+    const int c = 32 * kb + 8 * (l & 3) + 4 * h;
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(K + Lay::off(s0, c)));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(K + Lay::off(s0 + 16, c)));
+    return Arm::pack(__builtin_bit_cast(uint2, x), __builtin_bit_cast(uint2, y));
+  } else {
+    const int c = state_dim(t, l >> 2, l & 3);
+    typename Arm::F f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s = 32 * sb + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
+      f.v[e] = *(const float*)(K + Lay::off(s, c));
+    }
+    return f;
+  }
+}
+
+template <class Arm, int DK, int C, bool KDA, bool QF32>
+struct ScanLds {
+  typedef typename Arm::T T;
+  static constexpr int NBK = DK / 32, NBC = C / 32;
+  static constexpr int ESZV = QF32 ? 4 : 2;
+  static constexpr int RND = 256;
+  static constexpr int rnd(int x) { return (x + RND - 1) / RND * RND; }
+  // one chunk buffer: K (per-channel gate: e^G K, then e^{G_C - G} K), T fragments,
+  // 32 V columns (input type), row scalars
+  static constexpr int KY = 0;
+  static constexpr int KH = KY + (KDA ? rnd(OpLayout<Arm, DK>::template bytes<C>()) : 0);
+  static constexpr int TT = KH + rnd(OpLayout<Arm, DK>::template bytes<C>());
+  static constexpr int VV = TT + rnd(tile_elems(C) * (int)sizeof(T));
+  // raw rows for the gate sweep (64 entries each: one 4-byte copy instruction)
+  static constexpr int NDD = KDA ? (DK + 63) / 64 : 0;  // per-channel decay copies
+  static constexpr int GX = VV + rnd(C * 32 * ESZV);     // gate rows (per-head gate)
+  static constexpr int GB = GX + (KDA ? 0 : 256);        // beta rows
+  static constexpr int DC = GB + 256;                    // e^{G_C} per key channel
+  static constexpr int SC = DC + NDD * 256;
+  static constexpr int NSC = 4 * C + (KDA ? DK : 4);  // beta, beta e^G, e^{G_C-G}, e^G, decay
+  static constexpr int BUF = SC + rnd(NSC * 4);
+  // exchange, double-buffered by chunk parity: H_in and R fragments of both chain waves
+  static constexpr int FRAG = 64 * 8 * (int)sizeof(T);
+  static constexpr int HB = 0;
+  static constexpr int RO = HB + 2 * 2 * NBK * FRAG;
+  static constexpr int EXCH = RO + 2 * 2 * NBC * FRAG;
+  static constexpr int NBUF = 4 * BUF + EXCH <= 160 * 1024 ? 4 : (3 * BUF + EXCH <= 160 * 1024 ? 3 : 2);
+  // chunks the loader keeps complete ahead of the step that reads them: two with four
+  // buffers (the chain then reads the next chunk's K during the current step), else one
+  static constexpr int CL = NBUF == 4 ? 2 : 1;
+  static constexpr int BYTES = NBUF * BUF + EXCH;
+  // loader copy instructions per chunk
+  static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;
+  static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;
+  static constexpr int NDV = C * 32 * ESZV / 1024;
+  static constexpr int ND = (KDA ? 2 : 1) * NDK + NDT + NDV + (KDA ? 1 : 2) + NDD;
+  static_assert(NDK * 1024 == OpLayout<Arm, DK>::template bytes<C>(), "K copy granularity");
+  static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "T copy granularity");
+  static_assert(NDV * 1024 == C * 32 * ESZV, "V copy granularity");
+};
+
 template <class Arm, int DK, int C, bool KDA, bool QF32>
 __global__ __launch_bounds__(256) void gdn_scan(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
-  using Stage = ScanStageDims<Arm, DK, C, KDA, QF32>;
+  using Lay = OpLayout<Arm, DK>;
+  using SL = ScanLds<Arm, DK, C, KDA, QF32>;
   constexpr int NT = C / 16, NBC = C / 32, NTK = DK / 16, NBK = DK / 32;
-  constexpr int KP = DK + Arm::PAD, VP = 36;
-  constexpr int EPC = Stage::EPC, ESZ = QF32 ? 4 : 2;
-  constexpr int EPT = 16 / (int)sizeof(T);  // arm elements per 16 bytes
-  constexpr int NBUF = scan_nbuf<Arm, DK, C>(KDA);
-  constexpr size_t BUF = (scan_buf_bytes<Arm, DK, C>(KDA) + 255) / 256 * 256;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
-  const bool loader = wave >= 2;
-  const int u = wave & 1;            // compute: state unit; loader: loader index
-  const int ltid = tid & 127;        // loader thread index 0..127
+  constexpr int NBUF = SL::NBUF, LA = NBUF - 1;  // loader copies LA chunks ahead
+  constexpr int CL = SL::CL;                      // ... and keeps CL chunks complete ahead
+  constexpr bool PRE = CL >= 2;                   // chain prefetches the next chunk's K
+  constexpr int ESZV = SL::ESZV;
+  const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int DV = p.dv, nslice = DV / 32;
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  Give
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2): give
   // each XCD a contiguous range of (sequence, value head, slice) work items, so that the
-  // workgroups reading the same key head -- and the 4 slices of one value head -- share
-  // an L2 and hit in it.
+  // workgroups reading the same key head share an L2.
   int bid;
   {
     const int nb = (int)gridDim.x, per = nb / 8, rem = nb % 8;
@@ -795,27 +944,6 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
   const int h = bid % p.hv;
   const int n = bid / p.hv;
   const int kh = h / (p.hv / p.hk);
-  const int col0 = 32 * slice + 16 * u;  // compute waves: first value column
-
-  struct Buf {
-    T *Ks, *Kl, *Qs, *Ts, *Ps;
-    float *Vs, *sb_, *sbe, *seg, *sel, *sdec;
-  };
-  auto buf_at = [&](int b) __attribute__((always_inline)) {
-    Buf B;
-    B.Ks = (T*)(gdn_smem + b * BUF);      // K (per-head gate) or e^{G} K (per channel)
-    B.Kl = KDA ? B.Ks + C * KP : B.Ks;    // per channel: e^{G_C - G} K
-    B.Qs = B.Ks + (KDA ? 2 : 1) * C * KP; // Q or e^{G} Q
-    B.Ts = B.Qs + C * KP;
-    B.Ps = B.Ts + tile_elems(C);
-    B.Vs = (float*)(B.Ps + tile_elems(C));
-    B.sb_ = B.Vs + C * VP;  // beta
-    B.sbe = B.sb_ + C;      // beta e^{G}
-    B.seg = B.sbe + C;      // e^{G}
-    B.sel = B.seg + C;      // e^{G_C - G}
-    B.sdec = B.sel + C;     // e^{G_C} per key channel (per-channel gate) / [0] per-head gate
-    return B;
-  };
 
   int64_t s0, s1, slot0;
   if (p.varlen) {
@@ -827,367 +955,469 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
     s1 = s0 + p.seq_len;
     slot0 = (int64_t)n * p.chunks_per_seq;
   }
-  const int64_t nch = (s1 - s0 + C - 1) / C;
+  const int nch = (int)((s1 - s0 + C - 1) / C);
   uint32_t bad = 0;
 
-  // Loader staging: two register sets (chunks in flight).  Per-head gate: raw K and Q
-  // rows, gate and beta of row `lane` (first loader wave).  Per-channel gate: the gated
-  // operands from the sequence-parallel stage, beta, e^{G_C[d]}.
-  constexpr int NK = KDA ? 1 : Stage::NKQ, NG = KDA ? Stage::NG : 1;
-  u32x4 sk[2][NK], sq[2][NK], skg[2][NG], stt[2][Stage::NTP], spp[2][Stage::NTP], sv[2][Stage::NV];
-  float sg[2] = {0.f, 0.f}, sbt[2] = {0.f, 0.f}, sdc[2] = {0.f, 0.f};
-
-  // ---- loaders: global -> register set `rs` for chunk ci (branch-free: rows past the
-  //      chunk end re-read its last row, in bounds, and are zeroed by a select)
-  // Per-thread byte offsets inside a chunk (fixed), so that each load is a uniform chunk
-  // base plus a 32-bit offset.  Per-head gate: K/Q rows and V columns of this slice.
-  constexpr int KPR = DK / EPC;  // 16-byte pieces per K row
-  constexpr int VPR = 32 / EPC;  // 16-byte pieces per row of the 32 V columns
-  const int kstride = p.hk * DK * ESZ, vstride = p.hv * DV * ESZ;
-  const uint32_t koff0 = (uint32_t)((ltid / KPR) * kstride + (ltid % KPR) * 16);
-  const uint32_t voff0 = (uint32_t)((ltid / VPR) * vstride + (ltid % VPR) * 16);
-
-  // ---- loaders: global -> register set `rs` for chunk ci.  A partial last chunk reads
-  //      its last row again for the rows past its end (in bounds) and zeroes them.
-  auto issue = [&](int rs, int64_t ci) __attribute__((always_inline)) {
-    const int64_t t0 = s0 + ci * C;
-    const int L = (int)min64(C, s1 - t0);
-    const int64_t slot = slot0 + ci;
-    const bool full = L == C;  // uniform
-    if constexpr (!KDA) {
-      const char* kb = (const char*)p.k + (t0 * p.hk + kh) * (int64_t)(DK * ESZ);
-      const char* qb = (const char*)p.q + (t0 * p.hk + kh) * (int64_t)(DK * ESZ);
-      if (full) {
-#pragma unroll
-        for (int j = 0; j < Stage::NKQ; ++j) {
-          const uint32_t off = koff0 + (uint32_t)(j * (128 / KPR) * kstride);
-          sk[rs][j] = *(const u32x4*)(kb + off);
-          sq[rs][j] = *(const u32x4*)(qb + off);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < Stage::NKQ; ++j) {
-          const int r = (ltid + 128 * j) / KPR, c = (ltid + 128 * j) % KPR;
-          const uint32_t off = (uint32_t)((r < L ? r : L - 1) * kstride + c * 16);
-          const u32x4 a = *(const u32x4*)(kb + off), b = *(const u32x4*)(qb + off);
-          sk[rs][j] = (r < L) ? a : (u32x4)(0u);
-          sq[rs][j] = (r < L) ? b : (u32x4)(0u);
-        }
-      }
-      if (u == 0) {
-        const int rr = lane < L ? lane : L - 1;
-        const float x = p.g[(t0 + rr) * p.hv + h], b = p.beta[(t0 + rr) * p.hv + h];
-        sg[rs] = (lane < L) ? x : 0.f;
-        sbt[rs] = (lane < L) ? b : 0.f;
-      }
-    } else {
-      if (u == 0) {
-        const float b = p.beta[(t0 + (lane < L ? lane : L - 1)) * p.hv + h];
-        sbt[rs] = (lane < L) ? b : 0.f;
-      }
-      const u32x4* Gg = (const u32x4*)((const T*)p.Gws + (slot * p.hv + h) * (int64_t)(3 * C * DK));
-#pragma unroll
-      for (int j = 0; j < Stage::NG; ++j) skg[rs][j] = Gg[ltid + 128 * j];
-      if (ltid < DK) sdc[rs] = p.Dws[(slot * p.hv + h) * (int64_t)DK + ltid];
-    }
-    const u32x4* Tg = (const u32x4*)((const T*)p.Tws + (slot * p.hv + h) * (int64_t)tile_elems(C));
-    const u32x4* Pg = (const u32x4*)((const T*)p.Pws + (slot * p.hv + h) * (int64_t)tile_elems(C));
-#pragma unroll
-    for (int j = 0; j < Stage::NTP; ++j) {
-      stt[rs][j] = Tg[ltid + 128 * j];
-      spp[rs][j] = Pg[ltid + 128 * j];
-    }
-    const char* vb = (const char*)p.v + (t0 * p.hv + h) * (int64_t)(DV * ESZ) + 32 * slice * ESZ;
-    if (full) {
-#pragma unroll
-      for (int j = 0; j < Stage::NV; ++j)
-        sv[rs][j] = *(const u32x4*)(vb + voff0 + (uint32_t)(j * (128 / VPR) * vstride));
-    } else {
-#pragma unroll
-      for (int j = 0; j < Stage::NV; ++j) {
-        const int r = (ltid + 128 * j) / VPR, c = (ltid + 128 * j) % VPR;
-        const u32x4 a = *(const u32x4*)(vb + (uint32_t)((r < L ? r : L - 1) * vstride + c * 16));
-        sv[rs][j] = (r < L) ? a : (u32x4)(0u);
-      }
-    }
+  unsigned char* const ring = gdn_smem;
+  unsigned char* const exch = gdn_smem + NBUF * SL::BUF;
+  auto bufp = [&](int ci) __attribute__((always_inline)) { return ring + (ci % NBUF) * SL::BUF; };
+  auto scal = [&](int ci) __attribute__((always_inline)) { return (float*)(bufp(ci) + SL::SC); };
+  auto hb_at = [&](int par, int u, int kb) __attribute__((always_inline)) {
+    return (T*)(exch + SL::HB + ((par * 2 + u) * NBK + kb) * SL::FRAG) + lane * 8;
   };
+  auto ro_at = [&](int par, int u, int sb) __attribute__((always_inline)) {
+    return (T*)(exch + SL::RO + ((par * 2 + u) * NBC + sb) * SL::FRAG) + lane * 8;
+  };
+  // operand sources: row-major rows of DK arm elements, `ld` elements apart
+  const int64_t hvs = (int64_t)p.hv;
+  auto chunk_t0 = [&](int ci) __attribute__((always_inline)) { return s0 + (int64_t)ci * C; };
+  auto chunk_L = [&](int ci) __attribute__((always_inline)) { return (int)min64(C, s1 - chunk_t0(ci)); };
+  // K (and, per-channel gate, e^{G_C-G} K) and Q of chunk ci, row 0, and their row stride
+  auto src_k = [&](int ci, int which) __attribute__((always_inline)) -> const T* {
+    const int64_t slot = slot0 + ci;
+    if constexpr (KDA) return (const T*)p.Gws + ((slot * hvs + h) * 3 + which) * (int64_t)(C * DK);
+    else if (p.kq_ws) return (const T*)p.Kws + (slot * p.hk + kh) * (int64_t)(C * DK);
+    else return (const T*)p.k + (chunk_t0(ci) * p.hk + kh) * (int64_t)DK;
+  };
+  auto src_q = [&](int ci) __attribute__((always_inline)) -> const T* {
+    const int64_t slot = slot0 + ci;
+    if constexpr (KDA) return (const T*)p.Gws + ((slot * hvs + h) * 3 + 2) * (int64_t)(C * DK);
+    else if (p.kq_ws) return (const T*)p.Qws + (slot * p.hk + kh) * (int64_t)(C * DK);
+    else return (const T*)p.q + (chunk_t0(ci) * p.hk + kh) * (int64_t)DK;
+  };
+  const int kq_ld = (KDA || p.kq_ws) ? DK : p.hk * DK;
 
-  // ---- loaders: register set `rs` -> LDS buffer, plus the in-chunk gate sweep
-  auto commit = [&](int rs, const Buf& B) __attribute__((always_inline)) {
-    if constexpr (!KDA) {
+  if (wave == 3) {
+    // ------------------------------------------------------------- loader ----
+    // Only copies to LDS are issued here, one instruction per call, so the counts in
+    // the waits below are exact.
+    // per-lane byte offsets of this lane's pieces inside a full chunk (fixed), so that each
+    // copy of a full chunk is a uniform base plus a 32-bit offset
+    constexpr int VPR = 32 * ESZV / 16;  // pieces per V row
+    uint32_t koff[SL::NDK], voff[SL::NDV];
 #pragma unroll
-      for (int j = 0; j < Stage::NKQ; ++j) {
-        const int idx = ltid + 128 * j, r = idx / (DK / EPC), c = idx % (DK / EPC);
-        put16<Arm, QF32>(sk[rs][j], B.Ks + r * KP + c * EPC);
-        put16<Arm, QF32>(sq[rs][j], B.Qs + r * KP + c * EPC);
+    for (int k = 0; k < SL::NDK; ++k) {
+      int r, c;
+      Lay::piece_src(k * 64 + lane, r, c);
+      koff[k] = (uint32_t)((r * kq_ld + c) * (int)sizeof(T));
+    }
+#pragma unroll
+    for (int k = 0; k < SL::NDV; ++k) {
+      const int pc = k * 64 + lane;
+      voff[k] = (uint32_t)((pc / VPR) * p.hv * DV * ESZV + (pc % VPR) * 16);
+    }
+    auto issue = [&](int ci) __attribute__((always_inline)) {  // chunk ci -> its buffer
+      unsigned char* B = bufp(ci);
+      const int64_t t0 = chunk_t0(ci);
+      const int L = chunk_L(ci);
+      const char* vsrc = (const char*)p.v + (t0 * hvs + h) * (int64_t)(DV * ESZV) + 32 * slice * ESZV;
+      if (L == C) {  // uniform
+#pragma unroll
+        for (int w = 0; w < (KDA ? 2 : 1); ++w) {
+          const char* src = (const char*)src_k(ci, w);
+#pragma unroll
+          for (int k = 0; k < SL::NDK; ++k) dma16(src + koff[k], B + (KDA && w ? SL::KH : SL::KY) + k * 1024);
+        }
+#pragma unroll
+        for (int k = 0; k < SL::NDV; ++k) dma16(vsrc + voff[k], B + SL::VV + k * 1024);
+      } else {  // partial last chunk: rows past the end re-read its last row (in bounds)
+#pragma unroll
+        for (int w = 0; w < (KDA ? 2 : 1); ++w) {
+          const T* src = src_k(ci, w);
+#pragma unroll
+          for (int k = 0; k < SL::NDK; ++k) {
+            int r, c;
+            Lay::piece_src(k * 64 + lane, r, c);
+            dma16(src + (int64_t)(r < L ? r : L - 1) * kq_ld + c, B + (KDA && w ? SL::KH : SL::KY) + k * 1024);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < SL::NDV; ++k) {
+          const int pc = k * 64 + lane, r = pc / VPR, c = pc % VPR;
+          dma16(vsrc + (int64_t)(r < L ? r : L - 1) * hvs * DV * ESZV + c * 16, B + SL::VV + k * 1024);
+        }
       }
-      if (u == 0) {
-        const float G = wave_prefix_sum(sg[rs], lane);
-        const float GC = __shfl(G, C - 1, 64);
+      const char* tsrc = (const char*)p.Tws + ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
+#pragma unroll
+      for (int k = 0; k < SL::NDT; ++k) dma16(tsrc + (uint32_t)(k * 1024 + lane * 16), B + SL::TT + k * 1024);
+      // gate and beta of row min(lane, L - 1); the sweep masks rows past the end
+      const int64_t e = (t0 + (lane < L ? lane : L - 1)) * hvs + h;
+      if constexpr (!KDA) dma4(p.g + e, B + SL::GX);
+      dma4(p.beta + e, B + SL::GB);
+      if constexpr (KDA) {
+        const float* D = p.Dws + ((slot0 + ci) * hvs + h) * (int64_t)DK;
+#pragma unroll
+        for (int m = 0; m < SL::NDD; ++m) dma4(D + min(lane + 64 * m, DK - 1), B + SL::DC + m * 256);
+      }
+    };
+    auto sweep = [&](int ci) __attribute__((always_inline)) {  // scalars of chunk ci
+      const unsigned char* B = bufp(ci);
+      float* S = scal(ci);
+      const int L = chunk_L(ci);
+      const float bl = ((const float*)(B + SL::GB))[lane];
+      const float b = lane < L ? bl : 0.f;
+      bad |= flag_if(f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
+      if constexpr (!KDA) {
+        const float xl = ((const float*)(B + SL::GX))[lane];
+        const float x = lane < L ? xl : 0.f;
+        bad |= flag_if(f_nonfinite(x), GDN_ST_NONFINITE_INPUT);
+        bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
+        const float G = wave_prefix_sum_dpp(x);
+        const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
         if (lane < C) {
           const float eg = nexp(G);
-          B.sb_[lane] = sbt[rs];
-          B.sbe[lane] = sbt[rs] * eg;
-          B.seg[lane] = eg;
-          B.sel[lane] = nexp(GC - G);
+          S[lane] = b;
+          S[C + lane] = b * eg;
+          S[2 * C + lane] = nexp(GC - G);
+          S[3 * C + lane] = eg;
         }
-        if (lane == 0) B.sdec[0] = nexp(GC);
-      }
-    } else {
-      if (u == 0 && lane < C) B.sb_[lane] = sbt[rs];
-      if (ltid < DK) B.sdec[ltid] = sdc[rs];
-#pragma unroll
-      for (int j = 0; j < Stage::NG; ++j) {
-        const int e0 = (ltid + 128 * j) * EPT, m = e0 / (C * DK), r = (e0 / DK) % C, c = e0 % DK;
-        *(u32x4*)(B.Ks + (m * C + r) * KP + c) = skg[rs][j];  // Ks, Kl, Qs are consecutive
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < Stage::NTP; ++j) {  // fragments, verbatim
-      *(u32x4*)(B.Ts + (ltid + 128 * j) * EPT) = stt[rs][j];
-      *(u32x4*)(B.Ps + (ltid + 128 * j) * EPT) = spp[rs][j];
-    }
-#pragma unroll
-    for (int j = 0; j < Stage::NV; ++j) {
-      const int idx = ltid + 128 * j, r = idx / (32 / EPC), c = idx % (32 / EPC);
-      bad |= flag_if(nonfinite16<QF32>(sv[rs][j]), GDN_ST_NONFINITE_INPUT);
-      put16f<QF32>(sv[rs][j], B.Vs + r * VP + c * EPC);
-    }
-  };
-
-  // compute waves: fp32 state of this wave's 16 columns, rows d = 16 t + 4 g + ii
-  f32x4 H[NTK];
-  const int64_t hbase = ((int64_t)n * p.hv + h) * DK * (int64_t)DV;
-
-  // ---- compute waves: one chunk for this wave's 16 state columns.  Each phase's LDS
-  //      fragments are read into registers before its matrix products (the scheduling
-  //      barriers keep the reads batched), and the output products that do not depend
-  //      on the state chain fill the chain's dependency gaps.
-  auto compute = [&](const Buf& B, int64_t ci) __attribute__((always_inline)) {
-    const int64_t t0 = s0 + ci * C;
-    const int L = (int)min64(C, s1 - t0);
-    F HB[NBK];
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb) HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
-
-    // K and Q fragments
-    F kf[NBK][NT], qf[NBK][NT];
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        const T* krow = B.Ks + (16 * mt + i) * KP + 32 * kb + 4 * g;
-        kf[kb][mt] = Arm::row(krow, krow + 16);
-      }
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const T* qrow = B.Qs + (16 * nt + i) * KP + 32 * kb + 4 * g;
-        qf[kb][nt] = Arm::row(qrow, qrow + 16);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Y = K H_in (row tiles are independent accumulators, interleaved per k-block)
-    f32x4 Y[NT];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) Y[mt] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
-
-    // T fragments (lower triangle only) while O^T = H_in^T Q^T runs
-    F tf[NBC][NT];
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
-        if (32 * sb <= 16 * mt + 15) tf[sb][mt] = Arm::ld8(B.Ts + (tile_frag_index(mt, sb) * 64 + lane) * 8);
-    f32x4 O[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) O[nt] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) O[nt] = Arm::mma(HB[kb], qf[kb][nt], O[nt]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // X = beta V - beta e^{G} Y   (rows r = 16 mt + 4 g + ii)
-    f32x4 X[NT];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int r = 16 * mt + 4 * g + ii;
-        // per-channel gate: K already carries e^{G}, beta applies to the whole row
-        X[mt][ii] = KDA ? B.sb_[r] * (B.Vs[r * VP + 16 * u + i] - Y[mt][ii])
-                        : B.sb_[r] * B.Vs[r * VP + 16 * u + i] - B.sbe[r] * Y[mt][ii];
-      }
-    }
-    F XB[NBC];
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb) XB[sb] = Arm::acc(X[2 * sb], X[2 * sb + 1]);
-
-    // R = T X
-    f32x4 R[NT];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) R[mt] = zero4();
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
-        if (32 * sb <= 16 * mt + 15) R[mt] = Arm::mma(tf[sb][mt], XB[sb], R[mt]);
-
-    // Ktil^T fragments (transposing LDS reads) and P fragments
-    F ktf[NBC][NTK], pf[NBC][NT];
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-      for (int t = 0; t < NTK; ++t) ktf[sb][t] = Arm::col(B.Kl, KP, 32 * sb, 16 * t, lane);
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (32 * sb <= 16 * nt + 15) pf[sb][nt] = Arm::ld8(B.Ps + (tile_frag_index(nt, sb) * 64 + lane) * 8);
-    __builtin_amdgcn_sched_barrier(0);
-
-    F RO[NBC], RS[NBC];
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb) {
-      RO[sb] = Arm::acc(R[2 * sb], R[2 * sb + 1]);
-      if constexpr (KDA) {
-        RS[sb] = RO[sb];
+        if (lane == 0) S[4 * C] = nexp(GC);
       } else {
-        f32x4 lo, hi;
+        if (lane < C) S[lane] = b;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          lo[ii] = B.sel[32 * sb + 4 * g + ii] * R[2 * sb][ii];
-          hi[ii] = B.sel[32 * sb + 16 + 4 * g + ii] * R[2 * sb + 1][ii];
-        }
-        RS[sb] = Arm::acc(lo, hi);
+        for (int m = 0; m < SL::NDD; ++m)
+          if (lane + 64 * m < DK) S[4 * C + lane + 64 * m] = ((const float*)(B + SL::DC))[lane + 64 * m];
       }
+    };
+    auto check_v = [&](int ci) __attribute__((always_inline)) {  // Inf/NaN in V (LDS)
+      const u32x4* Vb = (const u32x4*)(bufp(ci) + SL::VV);
+      uint32_t nf = 0;
+#pragma unroll
+      for (int k = 0; k < SL::NDV; ++k) nf |= nf_bits16<QF32>(Vb[k * 64 + lane]);
+      bad |= flag_if(nf, GDN_ST_NONFINITE_INPUT);
+    };
+    // prologue: chunks 0 .. LA-1 copied, chunks 0 .. CL-1 complete and swept.  At most
+    // one chunk's copies (LA - CL <= 1) may stay in flight past a wait, so each wait
+    // allows either ND outstanding copies (when a later chunk was issued) or none.
+    static_assert(LA - CL <= 1, "one chunk in flight beyond the completed window");
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      if (j < nch) issue(j);
+    if (LA > CL && nch > LA - 1) wait_vm<(LA > CL ? SL::ND : 0)>();
+    else wait_vm<0>();
+#pragma unroll
+    for (int j = 0; j < CL; ++j)
+      if (j < nch) sweep(j);
+    __syncthreads();
+    for (int ci = 0; ci < nch; ++ci) {
+      const bool more = ci + LA < nch;
+      if (more) issue(ci + LA);
+      // chunk ci + CL complete: all copies but this step's
+      if (LA > CL && more) wait_vm<(LA > CL ? SL::ND : 0)>();
+      else wait_vm<0>();
+      if (ci + CL < nch) sweep(ci + CL);
+      check_v(ci);
+      __syncthreads();
     }
-
-    // H <- e^{G_C} H + Ktil^T R
-#pragma unroll
-    for (int t = 0; t < NTK; ++t) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) H[t][ii] *= KDA ? B.sdec[16 * t + 4 * g + ii] : B.sdec[0];
-    }
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-      for (int t = 0; t < NTK; ++t) H[t] = Arm::mma(ktf[sb][t], RS[sb], H[t]);
-
-    // O^T: gate scaling of the H_in part, then + R^T P^T
-    if constexpr (!KDA) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float e = B.seg[16 * nt + i];
-        O[nt][0] *= e; O[nt][1] *= e; O[nt][2] *= e; O[nt][3] *= e;
-      }
-    }
-#pragma unroll
-    for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (32 * sb <= 16 * nt + 15) O[nt] = Arm::mma(RO[sb], pf[sb][nt], O[nt]);
+  } else if (wave == 2) {
+    // ------------------------------------------------------------- output ----
+    // Q row fragments (contraction over the permuted key dims) and P fragments, loaded
+    // one chunk ahead of their use into two register sets.
+    constexpr int EPL = 8 / (16 / (int)sizeof(T));  // 16-byte loads per fragment
+    u32x4 qr[2][NT][NBK][EPL], pr[2][NBC][NT][EPL];
+    // per-lane byte offsets of this lane's Q pieces and O rows inside a full chunk
+    uint32_t qoff[NT], ooff[NT];
+    const int OSZ = p.o_f32 ? 4 : 2;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int r = 16 * nt + i;
-      if (r < L) {
-        const f32x4 o = O[nt];
-        bad |= flag_if(f_nonfinite(o[0]) | f_nonfinite(o[1]) | f_nonfinite(o[2]) | f_nonfinite(o[3]),
-                       GDN_ST_NONFINITE_OUTPUT);
-        const int64_t e = ((t0 + r) * p.hv + h) * (int64_t)DV + col0 + 4 * g;
-        if (p.o_f32) {
-          *(float4*)((float*)p.o + e) = (float4){o[0], o[1], o[2], o[3]};
-        } else {
-          const uint32_t w0 = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-          const uint32_t w1 = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
-          *(uint2*)((uint16_t*)p.o + e) = (uint2){w0, w1};
-        }
-      }
+      qoff[nt] = (uint32_t)(((16 * nt + i) * kq_ld + 8 * g) * (int)sizeof(T));
+      ooff[nt] = (uint32_t)(((16 * nt + i) * p.hv * DV + 8 * g) * OSZ);
     }
-  };
-
-  // ---- pipeline.  Each role runs its own loop (so the loaders' staging registers and
-  //      the compute waves' state never have to be live at the same time); both loops
-  //      execute the same sequence of barriers.  While the compute waves work on chunk ci
-  //      (LDS buffer ci&1), the loaders commit chunk ci+1 (register set (ci+1)&1, loaded
-  //      two chunks earlier) into the other buffer and start loading chunk ci+3 into the
-  //      set they just emptied.  Loops are unrolled by two so that buffer and register-set
-  //      indices are compile-time constants.
-  if (loader) {
-    if (nch > 0) {
-      issue(0, 0);
-      if (nch > 1) issue(1, 1);
-      commit(0, buf_at(0));
-      if (nch > 2) issue(0, 2);
-    }
-    __syncthreads();
-    auto lstep = [&](auto PAR, int64_t ci) __attribute__((always_inline)) {
-      constexpr int par = decltype(PAR)::value;  // ci & 1
-      constexpr int cur = NBUF == 2 ? par : 0;
-      constexpr int rs = par ^ 1;                // register set holding chunk ci+1
-      if (NBUF == 2) {
-        if (ci + 1 < nch) {
-          commit(rs, buf_at(cur ^ 1));
-          if (ci + 3 < nch) issue(rs, ci + 3);
-        }
-        __syncthreads();
+    auto load_q = [&](int ci, int set) __attribute__((always_inline)) {
+      const char* src = (const char*)src_q(ci);
+      const int L = chunk_L(ci);
+      if (L == C) {  // uniform
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) qr[set][nt][kb][x] = *(const u32x4*)(src + qoff[nt] + (32 * kb + x * (16 / (int)sizeof(T))) * (int)sizeof(T));
       } else {
-        __syncthreads();
-        if (ci + 1 < nch) {
-          commit(rs, buf_at(0));
-          if (ci + 3 < nch) issue(rs, ci + 3);
-          __syncthreads();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int r = 16 * nt + i;
+          const char* row = src + ((int64_t)(r < L ? r : L - 1) * kq_ld + 8 * g) * (int)sizeof(T);
+#pragma unroll
+          for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) qr[set][nt][kb][x] = *(const u32x4*)(row + (32 * kb + x * (16 / (int)sizeof(T))) * (int)sizeof(T));
         }
       }
     };
-    for (int64_t ci = 0; ci < nch; ci += 2) {
-      lstep(std::integral_constant<int, 0>{}, ci);
-      if (ci + 1 < nch) lstep(std::integral_constant<int, 1>{}, ci + 1);
+    auto load_p = [&](int ci, int set) __attribute__((always_inline)) {
+      const T* src = (const T*)p.Pws + ((slot0 + ci) * hvs + h) * (int64_t)tile_elems(C);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int sb = 0; sb < NBC; ++sb)
+          if (32 * sb <= 16 * nt + 15) {
+#pragma unroll
+            for (int x = 0; x < EPL; ++x)
+              pr[set][sb][nt][x] = *(const u32x4*)(src + (tile_frag_index(nt, sb) * 64 + lane) * 8 + x * (16 / (int)sizeof(T)));
+          }
+    };
+    auto frag = [&](const u32x4* raw) __attribute__((always_inline)) {
+      F f;
+      if constexpr (sizeof(T) == 2) f = __builtin_bit_cast(F, raw[0]);
+      else f = Arm::ld8((const T*)raw);
+      return f;
+    };
+    f32x4 OQ[2][NT];  // e^G (Q H_in) of the chunk in flight, both column halves
+    auto out_q = [&](int ci, int set) __attribute__((always_inline)) {
+      const int par = ci & 1;
+      const float* S = scal(ci);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        F hb[NBK];
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb) hb[kb] = Arm::ld8(hb_at(par, u, kb));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 o = zero4();
+#pragma unroll
+          for (int kb = 0; kb < NBK; ++kb) o = Arm::mma(hb[kb], frag(qr[set][nt][kb]), o);
+          const float e = KDA ? 1.f : S[3 * C + 16 * nt + i];
+          OQ[u][nt] = o * e;
+        }
+      }
+    };
+    auto out_p = [&](int ci, int set) __attribute__((always_inline)) {  // finish chunk ci
+      const int par = ci & 1;
+      const int64_t t0 = chunk_t0(ci);
+      const int L = chunk_L(ci);
+      // all products first (independent accumulators), then checks and stores
+      f32x4 o[2][NT];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        F ro[NBC];
+#pragma unroll
+        for (int sb = 0; sb < NBC; ++sb) ro[sb] = Arm::ld8(ro_at(par, u, sb));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          o[u][nt] = OQ[u][nt];
+#pragma unroll
+          for (int sb = 0; sb < NBC; ++sb)
+            if (32 * sb <= 16 * nt + 15) o[u][nt] = Arm::mma(ro[sb], frag(pr[set][sb][nt]), o[u][nt]);
+        }
+      }
+      // Inf/NaN in any row (rows past a partial chunk's end repeat finite inputs, so they
+      // are nonfinite only together with a real row)
+      uint32_t nf = 0;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) nf |= (__float_as_uint(o[u][nt][j]) & 0x7F800000u) + 0x00800000u;
+      bad |= flag_if(nf & 0x80000000u, GDN_ST_NONFINITE_OUTPUT);
+      // rows of this chunk: uniform base plus the lane's fixed row offsets
+      char* ob = (char*)p.o + ((t0 * hvs + h) * (int64_t)DV + 32 * slice) * OSZ;
+      // lane (i, g) of tile nt holds row 16 nt + i, slice columns 8 g .. 8 g + 7 (the
+      // first four from chain wave 0's quad, the next four from wave 1's)
+      auto st = [&](int nt) __attribute__((always_inline)) {
+        char* a = ob + ooff[nt];
+        const f32x4 v0 = o[0][nt], v1 = o[1][nt];
+        if (OSZ == 4) {
+          *(float4*)a = (float4){v0[0], v0[1], v0[2], v0[3]};
+          *(float4*)(a + 16) = (float4){v1[0], v1[1], v1[2], v1[3]};
+        } else {
+          const uint2 w0 = pack_bf16x4(v0), w1 = pack_bf16x4(v1);
+          *(u32x4*)a = (u32x4){w0.x, w0.y, w1.x, w1.y};
+        }
+      };
+      if (L == C) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st(nt);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          if (16 * nt + i < L) st(nt);
+      }
+    };
+    if (nch > 0) load_q(0, 0);
+    wait_vm<0>();
+    __syncthreads();
+    // step ci: finish chunk ci - 1 (P R part), start chunk ci (Q H_in part).  Register
+    // sets alternate by chunk parity; the loop is unrolled by two so they are constants.
+    auto ostep = [&](auto PAR, int ci) __attribute__((always_inline)) {
+      constexpr int cur = decltype(PAR)::value;  // ci & 1
+      // prefetches first; they complete before the barrier, so no load is outstanding
+      // across steps and the products below never wait on memory
+      if (ci + 1 < nch) load_q(ci + 1, cur ^ 1);
+      load_p(ci, cur);
+      if (ci > 0) out_p(ci - 1, cur ^ 1);
+      out_q(ci, cur);
+      wait_vm<0>();
+      __syncthreads();
+    };
+    for (int ci = 0; ci < nch; ci += 2) {
+      ostep(std::integral_constant<int, 0>{}, ci);
+      if (ci + 1 < nch) ostep(std::integral_constant<int, 1>{}, ci + 1);
+    }
+    if (nch > 0) {
+      if ((nch - 1) & 1) out_p(nch - 1, 1);
+      else out_p(nch - 1, 0);
     }
   } else {
-    // ---- compute waves: initial state
+    // -------------------------------------------------------------- chain ----
+    const int u = wave;
+    // this lane's state column inside the slice: the two chain waves own interleaved
+    // quads, so the output wave holds 8 consecutive columns of a row per lane
+    const int ccol = 8 * (i >> 2) + 4 * u + (i & 3);
+    const int col0 = 32 * slice + ccol;
+    const int64_t hbase = ((int64_t)n * p.hv + h) * DK * (int64_t)DV;
+    f32x4 H[NTK];
     if (p.h0) {
 #pragma unroll
       for (int t = 0; t < NTK; ++t)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) H[t][ii] = p.h0[hbase + (int64_t)(16 * t + 4 * g + ii) * DV + col0 + i];
-#pragma unroll
-      for (int t = 0; t < NTK; ++t)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          bad |= flag_if(f_nonfinite(H[t][ii]), GDN_ST_NONFINITE_INPUT);
+        for (int j = 0; j < 4; ++j) {
+          H[t][j] = p.h0[hbase + (int64_t)state_dim(t, g, j) * DV + col0];
+          bad |= flag_if(f_nonfinite(H[t][j]), GDN_ST_NONFINITE_INPUT);
+        }
     } else {
 #pragma unroll
       for (int t = 0; t < NTK; ++t) H[t] = zero4();
     }
-    __syncthreads();
-    auto cstep = [&](auto PAR, int64_t ci) __attribute__((always_inline)) {
-      constexpr int par = decltype(PAR)::value;
-      constexpr int cur = NBUF == 2 ? par : 0;
-      compute(buf_at(cur), ci);
-      __syncthreads();
-      if (NBUF == 1 && ci + 1 < nch) __syncthreads();
+    F HB[NBK];
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb) {
+      HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
+      Arm::st8(hb_at(0, u, kb), H[2 * kb], H[2 * kb + 1]);
+    }
+    F kf[NBK][NT];  // K row fragments of the chunk being processed
+    auto load_kf = [&](int ci) __attribute__((always_inline)) {
+      const unsigned char* B = bufp(ci) + SL::KY;
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) kf[kb][mt] = Arm::ld8((const T*)(B + Lay::off(16 * mt + i, 32 * kb + 8 * g)));
     };
-    for (int64_t ci = 0; ci < nch; ci += 2) {
-      cstep(std::integral_constant<int, 0>{}, ci);
-      if (ci + 1 < nch) cstep(std::integral_constant<int, 1>{}, ci + 1);
+    __syncthreads();
+    if (PRE && nch > 0) load_kf(0);
+    for (int ci = 0; ci < nch; ++ci) {
+      const unsigned char* B = bufp(ci);
+      const float* S = scal(ci);
+      const int par = ci & 1;
+      if (!PRE) load_kf(ci);
+      // Y = K H_in
+      f32x4 Y[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) Y[mt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
+      // operands of the rest of this chunk, read while the products run
+      float vv[NT][4];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * mt + 4 * g + j;
+          if constexpr (QF32) vv[mt][j] = *(const float*)(B + SL::VV + (r * 32 + ccol) * 4);
+          else vv[mt][j] = bf2f(*(const uint16_t*)(B + SL::VV + (r * 32 + ccol) * 2));
+        }
+      float4 b4[NT], e4[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        b4[mt] = *(const float4*)(S + 16 * mt + 4 * g);
+        if constexpr (!KDA) e4[mt] = *(const float4*)(S + C + 16 * mt + 4 * g);
+      }
+      F tf[NBC][NT];
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+          if (32 * sb <= 16 * mt + 15) tf[sb][mt] = Arm::ld8((const T*)(B + SL::TT) + (tile_frag_index(mt, sb) * 64 + lane) * 8);
+      // e^{G_C} H_in (the state's old part), off the product chain
+#pragma unroll
+      for (int t = 0; t < NTK; ++t) {
+        if constexpr (KDA) {
+          const float4 d4 = *(const float4*)(S + 4 * C + state_dim(t, g, 0));
+          H[t][0] *= d4.x; H[t][1] *= d4.y; H[t][2] *= d4.z; H[t][3] *= d4.w;
+        } else {
+          const float d = S[4 * C];
+          H[t][0] *= d; H[t][1] *= d; H[t][2] *= d; H[t][3] *= d;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // next chunk's K fragments (its buffer is complete one barrier early)
+      if (PRE && ci + 1 < nch) load_kf(ci + 1);
+      // X = beta V - beta e^G Y  (per-channel gate: K carries e^G, X = beta (V - Y))
+      F XB[NBC];
+      {
+        f32x4 X[NT];
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          const float bv[4] = {b4[mt].x, b4[mt].y, b4[mt].z, b4[mt].w};
+          if constexpr (KDA) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[mt][j] = bv[j] * (vv[mt][j] - Y[mt][j]);
+          } else {
+            const float ev[4] = {e4[mt].x, e4[mt].y, e4[mt].z, e4[mt].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[mt][j] = bv[j] * vv[mt][j] - ev[j] * Y[mt][j];
+          }
+        }
+#pragma unroll
+        for (int sb = 0; sb < NBC; ++sb) XB[sb] = Arm::acc(X[2 * sb], X[2 * sb + 1]);
+      }
+      // R = T X
+      f32x4 R[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) R[mt] = zero4();
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+          if (32 * sb <= 16 * mt + 15) R[mt] = Arm::mma(tf[sb][mt], XB[sb], R[mt]);
+      __builtin_amdgcn_sched_barrier(0);
+      // transposed K fragments for the state update
+      F ktf[NBC][NTK];
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int t = 0; t < NTK; ++t) ktf[sb][t] = kt_frag<Arm, DK>(B + SL::KH, sb, t, lane);
+      // R for the output wave; e^{G_C - G} R for the state update (per-channel gate: the
+      // factor is inside Ktil)
+      F RS[NBC];
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb) {
+        Arm::st8(ro_at(par, u, sb), R[2 * sb], R[2 * sb + 1]);
+        if constexpr (KDA) {
+          RS[sb] = Arm::acc(R[2 * sb], R[2 * sb + 1]);
+        } else {
+          const float4 a = *(const float4*)(S + 2 * C + 32 * sb + 4 * g);
+          const float4 c = *(const float4*)(S + 2 * C + 32 * sb + 16 + 4 * g);
+          f32x4 lo = R[2 * sb], hi = R[2 * sb + 1];
+          lo[0] *= a.x; lo[1] *= a.y; lo[2] *= a.z; lo[3] *= a.w;
+          hi[0] *= c.x; hi[1] *= c.y; hi[2] *= c.z; hi[3] *= c.w;
+          RS[sb] = Arm::acc(lo, hi);
+        }
+      }
+      // H <- e^{G_C} H_in + Ktil^T R
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int t = 0; t < NTK; ++t) H[t] = Arm::mma(ktf[sb][t], RS[sb], H[t]);
+      // H_in of the next chunk, for this wave and for the output wave
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb) {
+        HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
+        Arm::stf(hb_at(par ^ 1, u, kb), HB[kb]);
+      }
+      __syncthreads();
     }
     if (p.hT) {
 #pragma unroll
-      for (int t = 0; t < NTK; ++t) {
+      for (int t = 0; t < NTK; ++t)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int d = 16 * t + 4 * g + ii;
-          bad |= flag_if(f_nonfinite(H[t][ii]), GDN_ST_NONFINITE_OUTPUT);
-          p.hT[hbase + (int64_t)d * DV + col0 + i] = H[t][ii];
+        for (int j = 0; j < 4; ++j) {
+          bad |= flag_if(f_nonfinite(H[t][j]), GDN_ST_NONFINITE_OUTPUT);
+          p.hT[hbase + (int64_t)state_dim(t, g, j) * DV + col0] = H[t][j];
         }
-      }
     }
   }
   if (bad) atomicOr(p.status, bad);
@@ -1225,7 +1455,7 @@ gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   if (pl.run_scan) {
-    const size_t lds = scan_lds_bytes<Arm, DK, C>(KDA);
+    const size_t lds = ScanLds<Arm, DK, C, KDA, QF32>::BYTES;
     if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32>, lds)) return GDN_E_LAUNCH;
     const int64_t blocks = (int64_t)pl.n_seq * pl.hv * (pl.dv / 32);
     hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
