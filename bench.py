@@ -40,17 +40,19 @@ def algorithmic(spec, chunk):
     """Algorithmic bytes and flops of the two kernels for one layer.
 
     prep (per chunk and key head, then per value head of the group):
-      bytes: q, k chunk rows + g, beta rows + T and P tiles written (bf16)
+      bytes: q, k chunk rows + g, beta rows + T and P fragments written (bf16)
       flops: K K^T and Q K^T lower halves 2 C^2 dk per key head; solve C^3/3 per value head
     scan (per chunk and value head, 16 state columns per wave):
-      bytes: q, k rows (once per key head), v, o, g, beta, T and P tiles read; h0, hT
+      bytes: q, k rows (once per key head), v, o, g, beta, T and P fragments read; h0, hT
       flops: K.H and Ktil^T R  4 C dk dv;  Q.H  2 C dk dv;  P.R and T.X at half  2 C^2 dv / 2 each
     """
     T, hk, hv, dk, dv = spec.tokens, spec.hk, spec.hv, spec.dk, spec.dv
     n_seq = spec.n_seq
     nch = sum((l + chunk - 1) // chunk for l in spec.seq_lens)
     esz = 2
-    tile = chunk * chunk * esz
+    # T and P are stored as the lower-triangle operand fragments: 6 of the 8 16x32
+    # fragments of a 64 x 64 tile, both of a 32 x 32 tile
+    tile = sum(mt // 2 + 1 for mt in range(chunk // 16)) * 512 * esz
     qk = 2 * T * hk * dk * 2
     gb = 2 * T * hv * 4
     prep_bytes = qk + gb + 2 * nch * hv * tile
@@ -84,6 +86,66 @@ def traffic_from_profiles(kernel, digest):
         return None
     m = re.search(r"^%s\s+bytes_per_launch:\s*([0-9.eE+]+)" % re.escape(kernel), txt, re.M)
     return float(m.group(1)) if m else None
+
+
+def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds):
+    """Text summaries of rocprofv3 runs of this script: kernel durations (kernel trace) and
+    HBM bytes per launch (FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same
+    counter reads for the plain copy of --copy-probe, whose true bytes are known)."""
+    import csv
+    import glob
+    import numpy as np
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def short(name):
+        m = re.search(r"(gdn_\w+)<", name) or re.search(r"(gdn_\w+)\(", name)
+        if m:
+            return m.group(1)
+        if "AUnaryFunctor" in name or "MulFunctor" in name:
+            return "copy_probe"
+        return None
+
+    kt = rows(kt_dir, "*kernel_stats.csv")
+    lines = ["# rocprofv3 kernel trace: hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)",
+             "# command: " + cmds[0], "kernel  calls  avg_us  min_us  max_us  share_pct"]
+    for r in kt:
+        k = short(r["Name"])
+        if k and k != "copy_probe":
+            lines.append("%s  %s  %.2f  %.2f  %.2f  %s" % (k, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                        float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                                                        r["Percentage"]))
+    trace_txt = "\n".join(lines) + "\n"
+
+    per = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for r in rows(d, "*counter_collection.csv"):
+            k = short(r["Kernel_Name"])
+            if k and r["Counter_Name"] == cname:
+                per.setdefault((k, cname), []).append(float(r["Counter_Value"]))
+    probe_kib = PROBE_MIB * 1024.0
+    f_scale = probe_kib / np.mean(per[("copy_probe", "FETCH_SIZE")])
+    w_scale = probe_kib / np.mean(per[("copy_probe", "WRITE_SIZE")])
+    lines = ["# HBM traffic per launch from rocprofv3 counters: hybrid GDN layer",
+             "# commands: " + cmds[1], "#           " + cmds[2],
+             "# copy probe: %d MiB read and written; FETCH_SIZE read %.1f KiB (scale %.4f), "
+             "WRITE_SIZE %.1f KiB (scale %.4f)" % (PROBE_MIB, np.mean(per[("copy_probe", "FETCH_SIZE")]),
+                                                  f_scale, np.mean(per[("copy_probe", "WRITE_SIZE")]), w_scale),
+             "source_digest: %s" % source_digest()]
+    for k in sorted({k for k, _ in per if k != "copy_probe"}):
+        fk = np.mean(per[(k, "FETCH_SIZE")]) * f_scale
+        wk = np.mean(per[(k, "WRITE_SIZE")]) * w_scale
+        lines.append("%s fetch_bytes: %.6g" % (k, fk * 1024))
+        lines.append("%s write_bytes: %.6g" % (k, wk * 1024))
+        lines.append("%s bytes_per_launch: %.6g" % (k, (fk + wk) * 1024))
+    return trace_txt, "\n".join(lines) + "\n"
+
+
+PROBE_MIB = 256
 
 
 def cpu_baseline(inp, budget_s):
@@ -123,7 +185,28 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 output of this script and exit")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run a plain device copy of MIB MiB three times "
+                         "(reads and writes MIB MiB each): the reference for scaling HBM counters")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        cmds = ["cd /tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_kt -o kt -f csv -- "
+                "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu",
+                "cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/prof_fetch -o f -f csv -- "
+                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB,
+                "cd /tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/prof_write -o w -f csv -- "
+                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB]
+        trace_txt, traffic_txt = summarize_profiles(*args.summarize_profiles, cmds)
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        with open(os.path.join(ROOT, "profiles", "kernel_trace_hybrid.txt"), "w") as f:
+            f.write(trace_txt)
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic_hybrid.txt"), "w") as f:
+            f.write(traffic_txt)
+        print(trace_txt + traffic_txt)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
@@ -257,6 +340,15 @@ def main():
         "layer_hbm_frac": alg["layer_bytes"] / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "source_digest": digest,
     }
+    if args.copy_probe:
+        # one elementwise kernel per call: reads and writes copy_probe MiB of fp32
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        rec["copy_probe_bytes"] = n * 4
     if not args.no_cpu:
         log("timing the oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
