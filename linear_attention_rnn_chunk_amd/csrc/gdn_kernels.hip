@@ -559,9 +559,10 @@ __device__ __forceinline__ typename Arm::F frag_of(const u32x4* raw) {
 }
 
 // ----------------------------------------------------------- prep -------
-// Per-head gate: one wave per (chunk slot, value head), four per workgroup, no barrier.
-// The wave takes its K and Q operand fragments straight from global memory (the waves
-// of one key head's value heads are neighbours and share them through the caches),
+// Per-head gate: one wave per (chunk slot, value head), no barrier.  A workgroup holds up
+// to 4 value heads of one key head (blockDim = 64 * min(group, 4)), so the waves that read
+// the same K and Q rows run side by side on one CU and fetch them from HBM once.
+// The wave takes its K and Q operand fragments straight from global memory,
 // forms KK^T and (Q K^T) lower tiles on MFMA (contraction over dk in contiguous
 // 8-element pieces), runs its gate sweep, and hands the products to wave_tiles.
 template <class Arm, int DK, int C, bool QF32>
@@ -571,13 +572,15 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
   constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32;
   const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
-  const int64_t unit = (int64_t)blockIdx.x * 4 + w;
-  const int64_t slot = unit / p.hv;
-  const int h = (int)(unit - slot * p.hv);
+  const int group = p.hv / p.hk, wpb = blockDim.x >> 6, nblk = (group + wpb - 1) / wpb;
+  const int jb = blockIdx.x % nblk;
+  const int kh = (blockIdx.x / nblk) % p.hk;
+  const int64_t slot = blockIdx.x / (nblk * p.hk);
+  const int j = jb * wpb + w;  // value head inside the key head's group
   int n, L;
   int64_t t0;
-  if (slot >= p.max_slots || !locate_chunk(p, C, slot, n, t0, L)) return;
-  const int kh = h / (p.hv / p.hk);
+  if (j >= group || slot >= p.max_slots || !locate_chunk(p, C, slot, n, t0, L)) return;
+  const int h = kh * group + j;
   float* S = (float*)gdn_smem + w * SL::FLOATS;
   float* Gs = S + NTRI * kTile;
   float* Bs = Gs + C;
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
       Bs[lane] = b;
     }
   }
-  if (h % (p.hv / p.hk) == 0) {  // once per key head (wave-uniform)
+  if (j == 0) {  // once per key head (wave-uniform)
     uint32_t nf = 0;
 #pragma unroll
     for (int kb = 0; kb < NBK; ++kb)
@@ -784,11 +787,11 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
 //               Y = K H, X = beta V - beta e^G Y, R = T X, H <- e^{G_C} H + Ktil^T R
 //               with its fp32 state in MFMA accumulators
 //   wave 2      output, one chunk behind the chain: O = e^G (Q H_in) + P R for all 32
-//               columns, from H_in and R the chain waves leave in LDS; takes its Q and P
-//               operand fragments straight from global memory into registers
-//   wave 3      loader: copies K, T and V of chunk ci + NBUF - 1 global -> LDS directly
+//               columns, from H_in and R the chain waves leave in LDS and Q, P from the
+//               chunk buffer; it issues no global loads, only the O stores
+//   wave 3      loader: copies K, Q, P and V of chunk ci + NBUF - 1 global -> LDS directly
 //               (no register round trip) into a ring of NBUF chunk buffers, runs the
-//               in-chunk gate sweep one chunk ahead, checks V
+//               in-chunk gate sweep ahead, checks V
 // One workgroup barrier per chunk.
 //
 // State rows are stored permuted within each 32-key block: accumulator tile t = 2 kb + h,
@@ -797,33 +800,49 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
 // 32 kb + 8 g .. + 7, so the K and Q row fragments are single 16-byte pieces of their rows.
 __device__ __forceinline__ int state_dim(int t, int g, int j) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j; }
 
-// LDS layout of a C x DK operand matrix in row fragments: fragment (mt, kb) holds rows
-// 16 mt .. +15, key columns 32 kb .. +31; its lane slot (i, g) holds row 16 mt + i,
-// columns 32 kb + 8 g .. +7 (16 bytes bf16, 32 fp32).  Slot (i, g) sits at position
-// 4 i + (g ^ ((i >> 1) & 3)): a copy instruction's lanes 4i .. 4i+3 then read one 64-byte
-// piece of row i (coalesced), and the 8 lanes a 16-byte LDS read serves at once land on
-// 8 distinct bank groups.
+// LDS layout of a C x DK operand matrix, in 16-byte pieces.  A row of DK elements is NL
+// "lines" of LP pieces (LP = 8 pieces = one 128-byte cache line when a row is that long).
+// Lines are stored in blocks of RPI = 64 / LP rows: line (r, ln) at index
+// ((r / RPI) * NL + ln) * RPI + r % RPI, and inside it piece p sits at p ^ SW(r).  So one
+// copy instruction (64 lanes x 16 bytes) reads RPI whole cache lines, and the row fragment
+// of lane (i, g) -- row 16 mt + i, key columns 32 kb + 8 g .. +7 -- is one contiguous read;
+// the XOR by row spreads the 8 lanes a 16-byte LDS read serves over distinct bank groups.
 template <class Arm, int DK>
 struct OpLayout {
   typedef typename Arm::T T;
   static constexpr int NBK = DK / 32;
-  static constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
-  static constexpr int PPS = 8 / EPP;              // pieces per lane slot
+  static constexpr int EPP = 16 / (int)sizeof(T);  // elements per piece
+  static constexpr int PPS = 8 / EPP;              // pieces per 8-element lane slot
+  static constexpr int NP = DK / EPP;              // pieces per row
+  static constexpr int LP = NP < 8 ? NP : 8;       // pieces per line
+  static constexpr int NL = NP / LP;               // lines per row
+  static constexpr int RPI = 64 / LP;              // rows per copy instruction
   template <int C>
   static constexpr int bytes() { return C * DK * (int)sizeof(T); }
-  __device__ static __forceinline__ int slot_of(int i, int g) { return 4 * i + (g ^ ((i >> 1) & 3)); }
+  __device__ static __forceinline__ int sw(int r) { return ((r % RPI) * PPS) & (LP - 1); }
   // byte offset of element (r, c)
   __device__ static __forceinline__ int off(int r, int c) {
-    const int kb = c >> 5, g = (c >> 3) & 3, e = c & 7;
-    return (((((r >> 4) * NBK + kb) * 64 + slot_of(r & 15, g)) * PPS + e / EPP) * EPP + e % EPP) *
-           (int)sizeof(T);
+    const int pc = c / EPP, ln = pc / LP, p = pc % LP;
+    return ((((r / RPI) * NL + ln) * RPI + r % RPI) * LP + (p ^ sw(r))) * 16 + (c % EPP) * (int)sizeof(T);
   }
-  // (row, first column) of the elements the 16-byte piece number `pc` holds
+  // (row, first column) of the elements the 16-byte piece number `pc` of the layout holds
   __device__ static __forceinline__ void piece_src(int pc, int& r, int& c) {
-    const int x = pc % PPS, s = (pc / PPS) & 63, f = pc / (PPS * 64);
-    const int i = s >> 2, g = (s & 3) ^ ((i >> 1) & 3);
-    r = 16 * (f / NBK) + i;
-    c = 32 * (f % NBK) + 8 * g + x * EPP;
+    const int li = pc / LP, x = pc % LP;
+    const int rr = li % RPI, ln = (li / RPI) % NL, rb = li / (RPI * NL);
+    r = rb * RPI + rr;
+    c = (ln * LP + (x ^ sw(r))) * EPP;
+  }
+  // the 8-element lane slot starting at column c (a multiple of 8) of row r
+  __device__ static __forceinline__ typename Arm::F ld8(const unsigned char* base, int r, int c) {
+    if constexpr (PPS == 1) {
+      return Arm::ld8((const T*)(base + off(r, c)));
+    } else {
+      const float4 a = *(const float4*)(base + off(r, c)), b = *(const float4*)(base + off(r, c + 4));
+      typename Arm::F f;
+      f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+      f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+      return f;
+    }
   }
 };
 
@@ -880,39 +899,50 @@ struct ScanLds {
   typedef typename Arm::T T;
   static constexpr int NBK = DK / 32, NBC = C / 32;
   static constexpr int ESZV = QF32 ? 4 : 2;
-  static constexpr int RND = 256;
+  static constexpr int RND = 256, LDS_MAX = 160 * 1024;
   static constexpr int rnd(int x) { return (x + RND - 1) / RND * RND; }
-  // one chunk buffer: K (per-channel gate: e^G K, then e^{G_C - G} K), T fragments,
-  // 32 V columns (input type), row scalars
-  static constexpr int KY = 0;
-  static constexpr int KH = KY + (KDA ? rnd(OpLayout<Arm, DK>::template bytes<C>()) : 0);
-  static constexpr int TT = KH + rnd(OpLayout<Arm, DK>::template bytes<C>());
-  static constexpr int VV = TT + rnd(tile_elems(C) * (int)sizeof(T));
-  // raw rows for the gate sweep (64 entries each: one 4-byte copy instruction)
-  static constexpr int NDD = KDA ? (DK + 63) / 64 : 0;  // per-channel decay copies
-  static constexpr int GX = VV + rnd(C * 32 * ESZV);     // gate rows (per-head gate)
-  static constexpr int GB = GX + (KDA ? 0 : 256);        // beta rows
-  static constexpr int DC = GB + 256;                    // e^{G_C} per key channel
-  static constexpr int SC = DC + NDD * 256;
-  static constexpr int NSC = 4 * C + (KDA ? DK : 4);  // beta, beta e^G, e^{G_C-G}, e^G, decay
-  static constexpr int BUF = SC + rnd(NSC * 4);
+  static constexpr int OPB = rnd(OpLayout<Arm, DK>::template bytes<C>());  // one C x DK operand
   // exchange, double-buffered by chunk parity: H_in and R fragments of both chain waves
   static constexpr int FRAG = 64 * 8 * (int)sizeof(T);
   static constexpr int HB = 0;
   static constexpr int RO = HB + 2 * 2 * NBK * FRAG;
   static constexpr int EXCH = RO + 2 * 2 * NBC * FRAG;
-  static constexpr int NBUF = 4 * BUF + EXCH <= 160 * 1024 ? 4 : (3 * BUF + EXCH <= 160 * 1024 ? 3 : 2);
+  // one chunk buffer: K (per-channel gate: e^G K, then e^{G_C - G} K), Q (e^G Q) when it
+  // fits, P fragments, 32 V columns (input type), raw gate/beta rows, row scalars.  (T
+  // fragments go straight from global memory to the chain waves' registers.)
+  static constexpr int NDD = KDA ? (DK + 63) / 64 : 0;  // per-channel decay copies
+  static constexpr int NSC = 4 * C + (KDA ? DK : 4);    // beta, beta e^G, e^{G_C-G}, e^G, decay
+  static constexpr int buf_bytes(bool qr) {
+    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(tile_elems(C) * (int)sizeof(T)) + rnd(C * 32 * ESZV) +
+           (KDA ? 0 : 256) + 256 + NDD * 256 + rnd(NSC * 4);
+  }
+  // Q goes through the ring (copied like K, read from LDS by the output wave) when two
+  // buffers still fit; otherwise the output wave loads its Q fragments itself
+  static constexpr bool QR = 2 * buf_bytes(true) + EXCH <= LDS_MAX;
+  static constexpr int KY = 0;
+  static constexpr int KH = KY + (KDA ? OPB : 0);
+  static constexpr int QO = KH + OPB;
+  static constexpr int PP = QO + (QR ? OPB : 0);
+  static constexpr int VV = PP + rnd(tile_elems(C) * (int)sizeof(T));
+  static constexpr int GX = VV + rnd(C * 32 * ESZV);  // gate rows (per-head gate)
+  static constexpr int GB = GX + (KDA ? 0 : 256);     // beta rows
+  static constexpr int DC = GB + 256;                 // e^{G_C} per key channel
+  static constexpr int SC = DC + NDD * 256;
+  static constexpr int BUF = SC + rnd(NSC * 4);
+  static_assert(BUF == buf_bytes(QR), "buffer carve-up");
+  static constexpr int NBUF = 4 * BUF + EXCH <= LDS_MAX ? 4 : (3 * BUF + EXCH <= LDS_MAX ? 3 : 2);
+  static constexpr int BYTES = NBUF * BUF + EXCH;
+  static_assert(BYTES <= LDS_MAX, "scan LDS budget");
   // chunks the loader keeps complete ahead of the step that reads them: two with four
   // buffers (the chain then reads the next chunk's K during the current step), else one
   static constexpr int CL = NBUF == 4 ? 2 : 1;
-  static constexpr int BYTES = NBUF * BUF + EXCH;
   // loader copy instructions per chunk
   static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;
-  static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;
+  static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;  // P
   static constexpr int NDV = C * 32 * ESZV / 1024;
-  static constexpr int ND = (KDA ? 2 : 1) * NDK + NDT + NDV + (KDA ? 1 : 2) + NDD;
+  static constexpr int ND = ((KDA ? 2 : 1) + (QR ? 1 : 0)) * NDK + NDT + NDV + (KDA ? 1 : 2) + NDD;
   static_assert(NDK * 1024 == OpLayout<Arm, DK>::template bytes<C>(), "K copy granularity");
-  static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "T copy granularity");
+  static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "P copy granularity");
   static_assert(NDV * 1024 == C * 32 * ESZV, "V copy granularity");
 };
 
@@ -1013,22 +1043,24 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       const char* vsrc = (const char*)p.v + (t0 * hvs + h) * (int64_t)(DV * ESZV) + 32 * slice * ESZV;
       if (L == C) {  // uniform
 #pragma unroll
-        for (int w = 0; w < (KDA ? 2 : 1); ++w) {
-          const char* src = (const char*)src_k(ci, w);
+        for (int w = 0; w < (KDA ? 2 : 1) + (SL::QR ? 1 : 0); ++w) {
+          const char* src = (const char*)(w == (KDA ? 2 : 1) ? src_q(ci) : src_k(ci, w));
+          const int dst = w == (KDA ? 2 : 1) ? SL::QO : (KDA && w ? SL::KH : SL::KY);
 #pragma unroll
-          for (int k = 0; k < SL::NDK; ++k) dma16(src + koff[k], B + (KDA && w ? SL::KH : SL::KY) + k * 1024);
+          for (int k = 0; k < SL::NDK; ++k) dma16(src + koff[k], B + dst + k * 1024);
         }
 #pragma unroll
         for (int k = 0; k < SL::NDV; ++k) dma16(vsrc + voff[k], B + SL::VV + k * 1024);
       } else {  // partial last chunk: rows past the end re-read its last row (in bounds)
 #pragma unroll
-        for (int w = 0; w < (KDA ? 2 : 1); ++w) {
-          const T* src = src_k(ci, w);
+        for (int w = 0; w < (KDA ? 2 : 1) + (SL::QR ? 1 : 0); ++w) {
+          const T* src = w == (KDA ? 2 : 1) ? src_q(ci) : src_k(ci, w);
+          const int dst = w == (KDA ? 2 : 1) ? SL::QO : (KDA && w ? SL::KH : SL::KY);
 #pragma unroll
           for (int k = 0; k < SL::NDK; ++k) {
             int r, c;
             Lay::piece_src(k * 64 + lane, r, c);
-            dma16(src + (int64_t)(r < L ? r : L - 1) * kq_ld + c, B + (KDA && w ? SL::KH : SL::KY) + k * 1024);
+            dma16(src + (int64_t)(r < L ? r : L - 1) * kq_ld + c, B + dst + k * 1024);
           }
         }
 #pragma unroll
@@ -1037,9 +1069,9 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
           dma16(vsrc + (int64_t)(r < L ? r : L - 1) * hvs * DV * ESZV + c * 16, B + SL::VV + k * 1024);
         }
       }
-      const char* tsrc = (const char*)p.Tws + ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
+      const char* psrc = (const char*)p.Pws + ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
 #pragma unroll
-      for (int k = 0; k < SL::NDT; ++k) dma16(tsrc + (uint32_t)(k * 1024 + lane * 16), B + SL::TT + k * 1024);
+      for (int k = 0; k < SL::NDT; ++k) dma16(psrc + (uint32_t)(k * 1024 + lane * 16), B + SL::PP + k * 1024);
       // gate and beta of row min(lane, L - 1); the sweep masks rows past the end
       const int64_t e = (t0 + (lane < L ? lane : L - 1)) * hvs + h;
       if constexpr (!KDA) dma4(p.g + e, B + SL::GX);
@@ -1111,11 +1143,12 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
     }
   } else if (wave == 2) {
     // ------------------------------------------------------------- output ----
-    // Q row fragments (contraction over the permuted key dims) and P fragments, loaded
-    // one chunk ahead of their use into two register sets.
+    // P fragments, loaded one chunk ahead of their use into two register sets.  Q row
+    // fragments come from the chunk's LDS buffer, or, when Q does not fit in the ring,
+    // are loaded here one chunk ahead as well.
     constexpr int EPL = 8 / (16 / (int)sizeof(T));  // 16-byte loads per fragment
-    u32x4 qr[2][NT][NBK][EPL], pr[2][NBC][NT][EPL];
-    // per-lane byte offsets of this lane's Q pieces and O rows inside a full chunk
+    constexpr int NQR = SL::QR ? 1 : 2;              // register sets for Q (1 = unused)
+    u32x4 pr[2][NBC][NT][EPL], qr[NQR][SL::QR ? 1 : NT][NBK][EPL];
     uint32_t qoff[NT], ooff[NT];
     const int OSZ = p.o_f32 ? 4 : 2;
 #pragma unroll
@@ -1124,20 +1157,13 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       ooff[nt] = (uint32_t)(((16 * nt + i) * p.hv * DV + 8 * g) * OSZ);
     }
     auto load_q = [&](int ci, int set) __attribute__((always_inline)) {
-      const char* src = (const char*)src_q(ci);
-      const int L = chunk_L(ci);
-      if (L == C) {  // uniform
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-            for (int x = 0; x < EPL; ++x) qr[set][nt][kb][x] = *(const u32x4*)(src + qoff[nt] + (32 * kb + x * (16 / (int)sizeof(T))) * (int)sizeof(T));
-      } else {
+      if constexpr (!SL::QR) {
+        const char* src = (const char*)src_q(ci);
+        const int L = chunk_L(ci);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int r = 16 * nt + i;
-          const char* row = src + ((int64_t)(r < L ? r : L - 1) * kq_ld + 8 * g) * (int)sizeof(T);
+          const char* row = L == C ? src + qoff[nt] : src + ((int64_t)(r < L ? r : L - 1) * kq_ld + 8 * g) * (int)sizeof(T);
 #pragma unroll
           for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
@@ -1145,8 +1171,8 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
         }
       }
     };
-    auto load_p = [&](int ci, int set) __attribute__((always_inline)) {
-      const T* src = (const T*)p.Pws + ((slot0 + ci) * hvs + h) * (int64_t)tile_elems(C);
+    auto load_p = [&](int ci, int set) __attribute__((always_inline)) {  // LDS -> registers
+      const T* src = (const T*)(bufp(ci) + SL::PP);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -1167,6 +1193,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
     auto out_q = [&](int ci, int set) __attribute__((always_inline)) {
       const int par = ci & 1;
       const float* S = scal(ci);
+      const unsigned char* Qb = bufp(ci) + SL::QO;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         F hb[NBK];
@@ -1176,7 +1203,12 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
         for (int nt = 0; nt < NT; ++nt) {
           f32x4 o = zero4();
 #pragma unroll
-          for (int kb = 0; kb < NBK; ++kb) o = Arm::mma(hb[kb], frag(qr[set][nt][kb]), o);
+          for (int kb = 0; kb < NBK; ++kb) {
+            F qf;
+            if constexpr (SL::QR) qf = Lay::ld8(Qb, 16 * nt + i, 32 * kb + 8 * g);
+            else qf = frag(qr[set][SL::QR ? 0 : nt][kb]);
+            o = Arm::mma(hb[kb], qf, o);
+          }
           const float e = KDA ? 1.f : S[3 * C + 16 * nt + i];
           OQ[u][nt] = o * e;
         }
@@ -1244,11 +1276,11 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       constexpr int cur = decltype(PAR)::value;  // ci & 1
       // prefetches first; they complete before the barrier, so no load is outstanding
       // across steps and the products below never wait on memory
-      if (ci + 1 < nch) load_q(ci + 1, cur ^ 1);
+      if (ci + 1 < nch) load_q(ci + 1, SL::QR ? 0 : cur ^ 1);
       load_p(ci, cur);
       if (ci > 0) out_p(ci - 1, cur ^ 1);
-      out_q(ci, cur);
-      wait_vm<0>();
+      out_q(ci, SL::QR ? 0 : cur);
+      if constexpr (!SL::QR) wait_vm<0>();  // Q loads (stores are never waited on)
       __syncthreads();
     };
     for (int ci = 0; ci < nch; ci += 2) {
@@ -1287,16 +1319,40 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       Arm::st8(hb_at(0, u, kb), H[2 * kb], H[2 * kb + 1]);
     }
     F kf[NBK][NT];  // K row fragments of the chunk being processed
+    // T fragments: straight from global memory (stored in exactly this layout), two chunks
+    // ahead into two register sets (set = chunk parity); the chain issues no other global
+    // memory operation in its loop, so each step's wait leaves just the newest set in flight
+    constexpr int EPL = 8 / (16 / (int)sizeof(T));
+    constexpr int NTL = tile_frags(C) * EPL;  // T loads per chunk (lower fragments only)
+    u32x4 trs[2][NBC][NT][EPL];
+    auto load_t = [&](int ci, auto SET) __attribute__((always_inline)) {
+      auto& tr_ = trs[decltype(SET)::value];
+      const T* src = (const T*)p.Tws + ((slot0 + ci) * hvs + h) * (int64_t)tile_elems(C);
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+          if (32 * sb <= 16 * mt + 15) {
+#pragma unroll
+            for (int x = 0; x < EPL; ++x)
+              tr_[sb][mt][x] = *(const u32x4*)(src + (tile_frag_index(mt, sb) * 64 + lane) * 8 + x * (16 / (int)sizeof(T)));
+          }
+    };
     auto load_kf = [&](int ci) __attribute__((always_inline)) {
       const unsigned char* B = bufp(ci) + SL::KY;
 #pragma unroll
       for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt) kf[kb][mt] = Arm::ld8((const T*)(B + Lay::off(16 * mt + i, 32 * kb + 8 * g)));
+        for (int mt = 0; mt < NT; ++mt) kf[kb][mt] = Lay::ld8(B, 16 * mt + i, 32 * kb + 8 * g);
     };
+    if (nch > 0) load_t(0, std::integral_constant<int, 0>{});
+    if (nch > 1) load_t(1, std::integral_constant<int, 1>{});
+    wait_vm<0>();
     __syncthreads();
     if (PRE && nch > 0) load_kf(0);
-    for (int ci = 0; ci < nch; ++ci) {
+    auto cstep = [&](auto PAR, int ci) __attribute__((always_inline)) {
+      constexpr int cur = decltype(PAR)::value;  // ci & 1: T register set of this chunk
+      auto& tr_ = trs[cur];
       const unsigned char* B = bufp(ci);
       const float* S = scal(ci);
       const int par = ci & 1;
@@ -1330,7 +1386,10 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)
-          if (32 * sb <= 16 * mt + 15) tf[sb][mt] = Arm::ld8((const T*)(B + SL::TT) + (tile_frag_index(mt, sb) * 64 + lane) * 8);
+          if (32 * sb <= 16 * mt + 15) {
+            if constexpr (sizeof(T) == 2) tf[sb][mt] = __builtin_bit_cast(F, tr_[sb][mt][0]);
+            else tf[sb][mt] = Arm::ld8((const T*)tr_[sb][mt]);
+          }
       // e^{G_C} H_in (the state's old part), off the product chain
 #pragma unroll
       for (int t = 0; t < NTK; ++t) {
@@ -1408,7 +1467,19 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
         HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
         Arm::stf(hb_at(par ^ 1, u, kb), HB[kb]);
       }
+      // chunk ci + 2's T into this chunk's set; chunk ci + 1's (issued a step ago) must be
+      // complete at the barrier, chunk ci + 2's may stay in flight
+      if (ci + 2 < nch) {
+        load_t(ci + 2, PAR);
+        wait_vm<NTL>();
+      } else {
+        wait_vm<0>();
+      }
       __syncthreads();
+    };
+    for (int ci = 0; ci < nch; ci += 2) {
+      cstep(std::integral_constant<int, 0>{}, ci);
+      if (ci + 1 < nch) cstep(std::integral_constant<int, 1>{}, ci + 1);
     }
     if (p.hT) {
 #pragma unroll
@@ -1447,10 +1518,11 @@ gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
       const int64_t blocks = pl.max_slots * pl.hv;
       hipLaunchKernelGGL((gdn_prep_chan<Arm, DK, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     } else {
-      const size_t lds = 4 * SolveLds<C>::FLOATS * sizeof(float);
-      if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, lds)) return GDN_E_LAUNCH;
-      const int64_t blocks = (pl.max_slots * pl.hv + 3) / 4;
-      hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+      const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
+      const size_t lds = wpb * SolveLds<C>::FLOATS * sizeof(float);
+      if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
+      const int64_t blocks = pl.max_slots * pl.hk * nblk;
+      hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)blocks), dim3(64 * wpb), lds, st, prm);
     }
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
