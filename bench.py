@@ -9,8 +9,10 @@ seeded inputs, resident in HBM before timing).  Prints one JSON line.
 Per-kernel durations come from HIP events recorded on the library's stream
 around each stage call inside the timed loop (the step is issued as a PREP call
 then a SCAN call on the same workspace, which is exactly the work of one full
-call).  The oracle (fp64 token-serial, OpenMP) is timed on a bounded sample of
-the same workload on the host cores.
+call).  A 1 GiB scratch write before each step (outside its events) starts every
+step cache-cold; the headline is the median step, with the minimum and a
+warm-cache median beside it.  The oracle (fp64 token-serial, OpenMP) is timed on
+a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -184,6 +186,9 @@ def main():
     ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="before each timed step, write this much scratch memory (larger than "
+                         "the 256 MiB MALL and the L2s) so every step starts cache-cold; 0 = warm")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of this script and exit")
@@ -279,23 +284,34 @@ def main():
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
 
+    # Timed region: exactly `steps` layer steps between two device synchronisations.  Each
+    # step is preceded (outside its events) by a scratch write that evicts the caches, so
+    # the step time is cache-cold; the headline is the median step.
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record(stream)
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         step(evs[i])
-    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / args.steps
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    prep_v = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    scan_v = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_step = float(np.median(step_ms))
+    prep_ms, scan_ms = float(np.median(prep_v)), float(np.median(scan_v))
+    # warm-cache median for context (same work, no eviction in between)
+    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, args.steps // 2))]
+    for e in wev:
+        step(e)
+    torch.cuda.synchronize()
+    warm_ms = float(np.median([e[0].elapsed_time(e[2]) for e in wev]))
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
-    log("ms/step %.4f (prep %.4f, scan %.4f), wall %.3f s for %d steps"
-        % (ms_step, prep_ms, scan_ms, wall, args.steps))
+    log("ms/step %.4f median cold (min %.4f; prep %.4f, scan %.4f), warm %.4f, wall %.3f s for %d steps"
+        % (ms_step, step_ms.min(), prep_ms, scan_ms, warm_ms, wall, args.steps))
 
     alg = algorithmic(spec, chunk)
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if args.arm == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -337,6 +353,9 @@ def main():
                  "layer_frac": (alg["prep_flops"] + alg["scan_flops"]) / (ms_step * 1e-3)
                  / (peak_mfma * 1e12)},
         "kernels_ms": {"prep": prep_ms, "scan": scan_ms},
+        "timing": {"headline": "median cold-cache step (%d MiB scratch written before each step)"
+                               % args.flush_mib if args.flush_mib else "median warm step",
+                   "min_ms": float(step_ms.min()), "warm_median_ms": warm_ms},
         "layer_hbm_frac": alg["layer_bytes"] / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "source_digest": digest,
     }
