@@ -68,18 +68,21 @@ def algorithmic(spec, chunk):
                 scan_flops=scan_flops, chunks=nch, layer_bytes=layer_bytes)
 
 
-def source_digest():
+# the source file holding each workload's kernels and their launch code
+KERNEL_SOURCE = {"hybrid": "gdn_kernels.hip", "decode": "gdn_decode.hip"}
+
+
+def source_digest(label="hybrid"):
     h = hashlib.sha256()
-    for f in ("gdn_kernels.hip", "gdn_api.cpp", "gdn_internal.h"):
-        with open(os.path.join(ROOT, "linear_attention_rnn_chunk_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    with open(os.path.join(ROOT, "linear_attention_rnn_chunk_amd", "csrc", KERNEL_SOURCE[label]), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel, digest):
+def traffic_from_profiles(kernel, digest, label="hybrid"):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it was
-    taken on the current kernel sources (same digest); else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid.txt")
+    taken on the current kernel source (same digest); else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % label)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -90,7 +93,8 @@ def traffic_from_profiles(kernel, digest):
     return float(m.group(1)) if m else None
 
 
-def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds):
+def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds, label="hybrid",
+                       title="hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)"):
     """Text summaries of rocprofv3 runs of this script: kernel durations (kernel trace) and
     HBM bytes per launch (FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same
     counter reads for the plain copy of --copy-probe, whose true bytes are known)."""
@@ -113,7 +117,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds):
         return None
 
     kt = rows(kt_dir, "*kernel_stats.csv")
-    lines = ["# rocprofv3 kernel trace: hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)",
+    lines = ["# rocprofv3 kernel trace: " + title,
              "# command: " + cmds[0], "kernel  calls  avg_us  min_us  max_us  share_pct"]
     for r in kt:
         k = short(r["Name"])
@@ -132,12 +136,12 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds):
     probe_kib = PROBE_MIB * 1024.0
     f_scale = probe_kib / np.mean(per[("copy_probe", "FETCH_SIZE")])
     w_scale = probe_kib / np.mean(per[("copy_probe", "WRITE_SIZE")])
-    lines = ["# HBM traffic per launch from rocprofv3 counters: hybrid GDN layer",
+    lines = ["# HBM traffic per launch from rocprofv3 counters: " + title,
              "# commands: " + cmds[1], "#           " + cmds[2],
              "# copy probe: %d MiB read and written; FETCH_SIZE read %.1f KiB (scale %.4f), "
              "WRITE_SIZE %.1f KiB (scale %.4f)" % (PROBE_MIB, np.mean(per[("copy_probe", "FETCH_SIZE")]),
                                                   f_scale, np.mean(per[("copy_probe", "WRITE_SIZE")]), w_scale),
-             "source_digest: %s" % source_digest()]
+             "source_digest: %s" % source_digest(label)]
     for k in sorted({k for k, _ in per if k != "copy_probe"}):
         fk = np.mean(per[(k, "FETCH_SIZE")]) * f_scale
         wk = np.mean(per[(k, "WRITE_SIZE")]) * w_scale
@@ -177,6 +181,135 @@ def cpu_baseline(inp, budget_s):
                        "first %d tokens (%.1f s)" % (spec.hv, ntok, secs))
 
 
+def copy_probe(mib, dev):
+    """One elementwise kernel per call that reads and writes `mib` MiB of fp32, three
+    times: the known-size reference for scaling HBM counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return n * 4
+
+
+def decode_bytes(B, hk, hv, dk, dv):
+    """Algorithmic bytes of one step: per (sequence, value head) the fp32 state read and
+    written, v in and o out (bf16), gate and beta; per (sequence, key head) q and k."""
+    return B * hv * (2 * dk * dv * 4 + 2 * dv * 2 + 2 * 4) + B * hk * 2 * dk * 2
+
+
+def bench_decode(args):
+    """One-token steps of B sequences at the hybrid layer's shapes, states resident in
+    HBM, alternating between two state buffers (each step reads one, writes the other)."""
+    import numpy as np
+    import torch
+
+    from linear_attention_rnn_chunk_amd import gdn, inputs
+
+    B = args.decode
+    base = inputs.CONFIGS["hybrid"]
+    spec = inputs.Spec("decode", (1,) * B, base.hk, base.hv, base.dk, base.dv, gate_law="half",
+                       h0=True, packed=True, seed=2003)
+    log("generating decode inputs (%d sequences)" % B)
+    inp = inputs.make(spec)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def t(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v, g, beta, h0 = (t(getattr(inp, n)) for n in ("q", "k", "v", "g", "beta", "h0"))
+    prob = gdn.make_problem(B, B, 1, spec.hk, spec.hv, spec.dk, spec.dv, gdn.GATE_HEAD, 0, gdn.BF16,
+                            gdn.BF16)
+    o = torch.empty((B, spec.hv, spec.dv), dtype=torch.bfloat16, device=dev)
+    states = [h0, torch.empty_like(h0)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = gdn.decode_step_raw(prob, q, k, v, g, beta, states[i & 1], o, states[(i + 1) & 1], status,
+                                 stream.cuda_stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if rc:
+            raise gdn.GdnError(rc, "gdn_decode_step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if int(status.item()):
+        raise gdn.GdnStatusError(int(status.item()))
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, args.steps // 2))]
+    for i, e in enumerate(wev):
+        step(i, e)
+    torch.cuda.synchronize()
+    warm = float(np.median([e[0].elapsed_time(e[1]) for e in wev]))
+    if int(status.item()):
+        raise gdn.GdnStatusError(int(status.item()))
+    ms_step = float(np.median(ms))
+    nbytes = decode_bytes(B, spec.hk, spec.hv, spec.dk, spec.dv)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    log("decode B=%d: ms/step %.4f median cold (min %.4f), warm %.4f, %.0f GB/s"
+        % (B, ms_step, ms.min(), warm, gbs))
+    rec = {
+        "metric": "GDN one-token step: sequences/s (HV=48, d=128)",
+        "value": B / (ms_step * 1e-3),
+        "unit": "sequences/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "one-token step of %d sequences, 16 key / 48 value heads, dk=dv=128, "
+                               "bf16 q/k/v/o, fp32 state, per-head gate" % B, "sequences": B},
+        "roofline": {"bound": "hbm", "kernel": "gdn_decode", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("gdn_decode", source_digest("decode"), "decode"),
+                     "kernel_ms": ms_step, "algorithmic_bytes": nbytes},
+        "timing": {"headline": "median cold-cache step (%d MiB scratch written before each step)"
+                               % args.flush_mib if args.flush_mib else "median warm step",
+                   "min_ms": float(ms.min()), "warm_median_ms": warm},
+        "source_digest": source_digest("decode"),
+    }
+    if args.copy_probe:
+        rec["copy_probe_bytes"] = copy_probe(args.copy_probe, dev)
+    if not args.no_cpu:
+        import oracle
+        log("timing the oracle on a bounded sample")
+        n = min(B, 64)
+        sl = slice(0, n)
+        a64 = [inp.as_f64(x)[sl] for x in ("q", "k", "v", "g", "beta")] + [inp.h0[sl].astype(np.float64)]
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.serial_fwd(*a64, seq_start=np.arange(n + 1))
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= args.cpu_seconds:
+                break
+        rec["cpu_baseline"] = dict(value=reps * n / secs, unit="sequences/s",
+                                   cores=min(oracle.max_threads(), n * spec.hv), kind="oracle",
+                                   sample="fp64 token-serial oracle, one token of the first %d sequences "
+                                          "(all 48 value heads), repeated %d times (%.1f s)"
+                                          % (n, reps, secs))
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,23 +325,30 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of this script and exit")
+    ap.add_argument("--decode", type=int, default=0, metavar="B",
+                    help="time the one-token recurrent step instead: B sequences of the hybrid "
+                         "layer's heads, each continuing from its own state; prints its own line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of MIB MiB three times "
                          "(reads and writes MIB MiB each): the reference for scaling HBM counters")
     args = ap.parse_args()
 
     if args.summarize_profiles:
+        label = "decode" if args.decode else "hybrid"
+        extra = " --decode %d" % args.decode if args.decode else ""
+        title = ("one-token step, %d sequences of the hybrid layer (16/48 heads, d=128)" % args.decode
+                 if args.decode else "hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)")
         cmds = ["cd /tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_kt -o kt -f csv -- "
-                "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu",
+                "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu" + extra,
                 "cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/prof_fetch -o f -f csv -- "
-                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB,
+                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB + extra,
                 "cd /tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/prof_write -o w -f csv -- "
-                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB]
-        trace_txt, traffic_txt = summarize_profiles(*args.summarize_profiles, cmds)
+                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB + extra]
+        trace_txt, traffic_txt = summarize_profiles(*args.summarize_profiles, cmds, label, title)
         os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-        with open(os.path.join(ROOT, "profiles", "kernel_trace_hybrid.txt"), "w") as f:
+        with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.txt" % label), "w") as f:
             f.write(trace_txt)
-        with open(os.path.join(ROOT, "profiles", "hbm_traffic_hybrid.txt"), "w") as f:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % label), "w") as f:
             f.write(traffic_txt)
         print(trace_txt + traffic_txt)
         return
@@ -226,6 +366,9 @@ def main():
     if not os.path.exists(gdn.LIBRARY_PATH):
         import __graft_entry__
         __graft_entry__.build()
+
+    if args.decode:
+        return bench_decode(args)
 
     spec = inputs.CONFIGS[args.config]
     chunk = args.chunk or spec.chunk
@@ -320,8 +463,8 @@ def main():
     dom_bytes = alg[dom + "_bytes"]
     achieved_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     kernel_name = "gdn_scan" if dom == "scan" else "gdn_prep"
-    digest = source_digest()
-    traffic = traffic_from_profiles(kernel_name, digest)
+    digest = source_digest("hybrid")
+    traffic = traffic_from_profiles(kernel_name, digest, "hybrid")
     tokens_s = spec.tokens / (ms_step * 1e-3)
 
     rec = {
@@ -360,14 +503,7 @@ def main():
         "source_digest": digest,
     }
     if args.copy_probe:
-        # one elementwise kernel per call: reads and writes copy_probe MiB of fp32
-        n = args.copy_probe * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        rec["copy_probe_bytes"] = n * 4
+        rec["copy_probe_bytes"] = copy_probe(args.copy_probe, dev)
     if not args.no_cpu:
         log("timing the oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

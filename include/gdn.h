@@ -24,8 +24,9 @@
  *     allocates and frees nothing and keeps no global state.
  *   - Tensors are dense, row-major, last dimension contiguous, no padding.
  *   - Host-detected errors return synchronously and launch nothing.
- *   - gdn_chunk_fwd is asynchronous on `stream`; device-detected conditions are
- *     OR-ed into *status (sticky), which the caller reads after synchronising.
+ *   - gdn_chunk_fwd and gdn_decode_step are asynchronous on `stream`; device-detected
+ *     conditions are OR-ed into *status (sticky), which the caller reads after
+ *     synchronising.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -121,6 +122,38 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
                          const float* g, const float* beta, const float* h0,
                          const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_decode_step -- one recurrent step: one new token for each of n_seq sequences,
+ * continuing from their states (the hT of a prefill, or the h_out of an earlier step).
+ * It is the same rule as above for a single token, evaluated directly:
+ *     H_out = D H_in + k (beta (v - (D H_in)^T k))^T,   o = H_out^T q
+ * (the stratat.com page, section "What this is", at T = 1; the K-first immutable input
+ * state and separate next state follow the logismos issue #46 page, "Verified
+ * implementation boundary" and the Sep 8 activity).  Every step runs in fp32.
+ *   p           n_seq sequences, seq_len == 1, total_tokens == n_seq; hk, hv, dk, dv,
+ *               gate, qkv_dtype and o_dtype as for gdn_chunk_fwd; chunk, arm, compose
+ *               and stages are not read
+ *   q, k        [n_seq][hk][dk]   qkv_dtype, 4-byte aligned
+ *   v           [n_seq][hv][dv]   qkv_dtype, 16-byte (fp32) / 8-byte (bf16) aligned
+ *   g           fp32 natural-log decay, [n_seq][hv] or [n_seq][hv][dk]
+ *   beta        fp32 [n_seq][hv]
+ *   h_in        fp32 [n_seq][hv][dk][dv] states before the token, or NULL for zeros;
+ *               never written; 16-byte aligned
+ *   o           [n_seq][hv][dv] o_dtype, aligned as v
+ *   h_out       fp32 [n_seq][hv][dk][dv] states after the token, 16-byte aligned; must
+ *               not overlap h_in (or any other argument)
+ *   status      one uint32 on the device, zeroed by the caller; device bits OR-ed in:
+ *               NONFINITE_INPUT (q, k, v, g, beta, h_in), GATE_DOMAIN (g > 0; a
+ *               single step has no lower limit on a per-channel gate), NONFINITE_OUTPUT
+ *   stream      a hipStream_t (NULL = the default stream)
+ * No workspace.  Returns GDN_OK after enqueueing one kernel, or a host error
+ * (GDN_E_NULL, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_ALIAS, GDN_E_LAUNCH) with nothing
+ * launched.
+ */
+gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* h_in, void* o,
+                           float* h_out, uint32_t* status, void* stream);
 
 /* Static text for a host return code. */
 const char* gdn_error_string(int32_t code);

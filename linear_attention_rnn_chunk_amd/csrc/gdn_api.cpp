@@ -196,6 +196,64 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   return gdn::launch(pl, prm, stream);
 }
 
+gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* h_in, void* o,
+                           float* h_out, uint32_t* status, void* stream) {
+  if (!p) return GDN_E_NULL;
+  if (p->n_seq < 0 || p->hk < 1 || p->hv < 1 || p->seq_len != 1 || p->total_tokens != p->n_seq)
+    return GDN_E_SHAPE;
+  if (p->hv % p->hk != 0) return GDN_E_UNSUPPORTED;
+  if (!(p->dk == 32 || p->dk == 64 || p->dk == 128)) return GDN_E_UNSUPPORTED;
+  if (!(p->dv == 32 || p->dv == 64 || p->dv == 128)) return GDN_E_UNSUPPORTED;
+  if (p->gate != GDN_GATE_HEAD && p->gate != GDN_GATE_KEY_CHANNEL) return GDN_E_UNSUPPORTED;
+  if (p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_F32) return GDN_E_UNSUPPORTED;
+  if (p->o_dtype != GDN_BF16 && p->o_dtype != GDN_F32) return GDN_E_UNSUPPORTED;
+  if ((int64_t)p->n_seq * p->hv * (p->dv / 32) > INT32_MAX) return GDN_E_UNSUPPORTED;
+  if (!status) return GDN_E_NULL;
+  if (p->n_seq > 0 && (!q || !k || !v || !g || !beta || !o || !h_out)) return GDN_E_NULL;
+  const bool qf = p->qkv_dtype == GDN_F32, of = p->o_dtype == GDN_F32;
+  // vector accesses: 4 state columns (16 bytes), 4 v / o elements (8 or 16 bytes)
+  if (!gdn::aligned(q, 4) || !gdn::aligned(k, 4) || !gdn::aligned(v, qf ? 16 : 8) ||
+      !gdn::aligned(o, of ? 16 : 8) || !gdn::aligned(g, 4) || !gdn::aligned(beta, 4) ||
+      !gdn::aligned(h_in, 16) || !gdn::aligned(h_out, 16) || !gdn::aligned(status, 4))
+    return GDN_E_UNSUPPORTED;
+  const size_t N = (size_t)p->n_seq, qsz = qf ? 4 : 2, osz = of ? 4 : 2;
+  const size_t nq = N * p->hk * p->dk * qsz, nv = N * p->hv * p->dv * qsz;
+  const size_t ng = N * p->hv * (p->gate == GDN_GATE_KEY_CHANNEL ? p->dk : 1) * 4, nb = N * p->hv * 4;
+  const size_t nh = N * p->hv * p->dk * p->dv * 4, no = N * p->hv * p->dv * osz;
+  struct R {
+    const void* p;
+    size_t n;
+  };
+  const R ins[] = {{q, nq}, {k, nq}, {v, nv}, {g, ng}, {beta, nb}, {h_in, nh}};
+  const R outs[] = {{o, no}, {h_out, nh}, {status, 4}};
+  for (const R& a : outs) {
+    for (const R& b : ins)
+      if (gdn::overlap(a.p, a.n, b.p, b.n)) return GDN_E_ALIAS;
+    for (const R& b : outs)
+      if (&a != &b && gdn::overlap(a.p, a.n, b.p, b.n)) return GDN_E_ALIAS;
+  }
+  if (p->n_seq == 0) return GDN_OK;
+  gdn::DecodeParams prm;
+  memset(&prm, 0, sizeof(prm));
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.g = g;
+  prm.beta = beta;
+  prm.h_in = h_in;
+  prm.o = o;
+  prm.h_out = h_out;
+  prm.status = status;
+  prm.n_seq = p->n_seq;
+  prm.hk = p->hk;
+  prm.hv = p->hv;
+  prm.dv = p->dv;
+  prm.qkv_f32 = qf;
+  prm.o_f32 = of;
+  return gdn::launch_decode(prm, p->dk, p->gate == GDN_GATE_KEY_CHANNEL, stream);
+}
+
 const char* gdn_error_string(int32_t code) {
   switch (code) {
     case GDN_OK: return "ok";

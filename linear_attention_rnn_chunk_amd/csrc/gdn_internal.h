@@ -62,7 +62,23 @@ struct Params {
   int64_t max_slots;
 };
 
+// Arguments of the one-token recurrent step (by value).
+struct DecodeParams {
+  const void* q;      // [n_seq][hk][dk]
+  const void* k;      // [n_seq][hk][dk]
+  const void* v;      // [n_seq][hv][dv]
+  const float* g;     // [n_seq][hv] or [n_seq][hv][dk]
+  const float* beta;  // [n_seq][hv]
+  const float* h_in;  // [n_seq][hv][dk][dv] or null (zeros)
+  void* o;            // [n_seq][hv][dv]
+  float* h_out;       // [n_seq][hv][dk][dv]
+  uint32_t* status;
+  int32_t n_seq, hk, hv, dv;
+  int32_t qkv_f32, o_f32;
+};
+
 gdn_status make_plan(const gdn_problem* p, Plan* plan);
+gdn_status launch_decode(const DecodeParams& prm, int dk, bool per_channel_gate, void* stream);
 gdn_status launch(const Plan& plan, const Params& prm, void* stream);
 
 }  // namespace gdn

@@ -29,8 +29,8 @@ COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED = 0, 1, 2
 STAGE_ALL, STAGE_PREP, STAGE_SCAN = 0, 1, 2
 
 # every symbol include/gdn.h declares
-EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_chunk_fwd", "gdn_error_string",
-           "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
+           "gdn_error_string", "gdn_status_string", "gdn_abi_version")
 
 
 class Problem(ctypes.Structure):
@@ -79,6 +79,8 @@ def load():
             lib.gdn_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.c_size_t, vp]
             lib.gdn_chunk_fwd.restype = ctypes.c_int
+            lib.gdn_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.gdn_decode_step.restype = ctypes.c_int
             lib.gdn_error_string.argtypes = [ctypes.c_int32]
             lib.gdn_error_string.restype = ctypes.c_char_p
             lib.gdn_status_string.argtypes = [ctypes.c_uint32]
@@ -209,3 +211,61 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm
     if squeeze:
         o = o.squeeze(0)
     return o, hT, status
+
+
+def decode_step_raw(prob: Problem, q, k, v, g, beta, h_in, o, h_out, status, stream=None) -> int:
+    """Direct call of gdn_decode_step with caller-owned tensors; returns the host code."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load().gdn_decode_step(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h_in), _ptr(o),
+        _ptr(h_out), _ptr(status), ctypes.c_void_p(int(stream))))
+
+
+def decode_step(q, k, v, g, beta, h_in=None, *, o_dtype: Optional[torch.dtype] = None,
+                h_out: Optional[torch.Tensor] = None, check: bool = True):
+    """One recurrent step (one new token per sequence) on the current device and stream.
+
+    q, k [B, HK, DK]; v [B, HV, DV]; g [B, HV] (per-head gate) or [B, HV, DK]
+    (per-key-channel gate); beta [B, HV]; h_in [B, HV, DK, DV] float32 or None (zeros).
+    Returns (o [B, HV, DV], h_out [B, HV, DK, DV] float32, status int32[1] on the
+    device); h_in is never written.  With ``check`` the stream is synchronised and any
+    device status bit raises GdnStatusError.
+    """
+    B, HK, DK = q.shape
+    HV, DV = v.shape[1], v.shape[2]
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share dtype bfloat16 or float32")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("h_in", h_in),
+                    ("h_out", h_out)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous device tensor" % name)
+    if k.shape != q.shape or v.shape[0] != B or beta.shape != (B, HV):
+        raise ValueError("inconsistent q/k/v/beta shapes")
+    if g.shape == (B, HV):
+        gate = GATE_HEAD
+    elif g.shape == (B, HV, DK):
+        gate = GATE_KEY_CHANNEL
+    else:
+        raise ValueError("g must be [B, HV] or [B, HV, DK]")
+    for name, t in (("h_in", h_in), ("h_out", h_out)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, HV, DK, DV)):
+            raise ValueError("%s must be float32 [B, HV, DK, DV]" % name)
+    odt = o_dtype or q.dtype
+    prob = make_problem(B, B, 1, HK, HV, DK, DV, gate, 0, _DT[q.dtype], _DT[odt])
+    dev = q.device
+    o = torch.empty((B, HV, DV), dtype=odt, device=dev)
+    if h_out is None:
+        h_out = torch.empty((B, HV, DK, DV), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    rc = decode_step_raw(prob, q, k, v, g, beta, h_in, o, h_out, status)
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_decode_step")
+    if check:
+        torch.cuda.current_stream().synchronize()
+        bits = int(status.item()) & 0xFFFFFFFF
+        if bits:
+            raise GdnStatusError(bits)
+    return o, h_out, status

@@ -153,3 +153,65 @@ def test_empty_problem_returns_ok_without_device_work():
     rc = lib.gdn_chunk_fwd(ctypes.byref(prob), None, None, None, None, None, None, None, None,
                            None, st, None, ctypes.c_size_t(0), None)
     assert rc == gdn.GDN_OK
+
+
+def D(**kw):
+    base = dict(n_seq=4, total_tokens=4, seq_len=1, hk=2, hv=6, dk=128, dv=128)
+    base.update(kw)
+    return gdn.make_problem(**base)
+
+
+def _daddrs(prob, qkv=2, osz=2):
+    N, hk, hv, dk, dv = prob.n_seq, prob.hk, prob.hv, prob.dk, prob.dv
+    gw = dk if prob.gate == gdn.GATE_KEY_CHANNEL else 1
+    sizes = dict(q=N * hk * dk * qkv, k=N * hk * dk * qkv, v=N * hv * dv * qkv, g=N * hv * gw * 4,
+                 beta=N * hv * 4, h_in=N * hv * dk * dv * 4, o=N * hv * dv * osz,
+                 h_out=N * hv * dk * dv * 4, status=4)
+    a, out = BASE, {}
+    for k_, n in sizes.items():
+        out[k_] = a
+        a += (n + 4095) // 4096 * 4096 + 4096
+    return out
+
+
+def _dcall(prob, a, **override):
+    args = dict(a)
+    args.update(override)
+    vp = ctypes.c_void_p
+    return gdn.load().gdn_decode_step(
+        ctypes.byref(prob), vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["g"]),
+        vp(args["beta"]), vp(args["h_in"]), vp(args["o"]), vp(args["h_out"]), vp(args["status"]),
+        vp(0))
+
+
+def test_decode_refusals_on_host():
+    a = _daddrs(D())
+    lib = gdn.load()
+    assert lib.gdn_decode_step(None, *([None] * 10)) == gdn.GDN_E_NULL
+    assert _dcall(D(seq_len=2, total_tokens=8), a) == gdn.GDN_E_SHAPE     # not one token each
+    assert _dcall(D(total_tokens=5), a) == gdn.GDN_E_SHAPE
+    assert _dcall(D(n_seq=-1, total_tokens=-1), a) == gdn.GDN_E_SHAPE
+    assert _dcall(D(hv=5), a) == gdn.GDN_E_UNSUPPORTED
+    assert _dcall(D(dk=96), a) == gdn.GDN_E_UNSUPPORTED
+    assert _dcall(D(dv=16), a) == gdn.GDN_E_UNSUPPORTED
+    assert _dcall(D(gate=3), a) == gdn.GDN_E_UNSUPPORTED
+    assert _dcall(D(o_dtype=5), a) == gdn.GDN_E_UNSUPPORTED
+    assert _dcall(D(), a, status=None) == gdn.GDN_E_NULL
+    assert _dcall(D(), a, h_out=None) == gdn.GDN_E_NULL
+    assert _dcall(D(), a, v=None) == gdn.GDN_E_NULL
+    assert _dcall(D(), a, h_in=a["h_in"] + 8) == gdn.GDN_E_UNSUPPORTED    # not 16-aligned
+    assert _dcall(D(), a, v=a["v"] + 4) == gdn.GDN_E_UNSUPPORTED          # bf16 v: 8-aligned
+    assert _dcall(D(), a, h_out=a["h_in"]) == gdn.GDN_E_ALIAS             # in-place state
+    assert _dcall(D(), a, h_out=a["h_in"] + 4096) == gdn.GDN_E_ALIAS      # partial overlap
+    assert _dcall(D(), a, o=a["q"]) == gdn.GDN_E_ALIAS
+    assert _dcall(D(), a, status=a["o"]) == gdn.GDN_E_ALIAS
+    # chunk, arm, compose and stages are not read by the step
+    assert _dcall(D(n_seq=0, total_tokens=0, chunk=16, arm=7, compose=9), a) == gdn.GDN_OK
+
+
+def test_decode_empty_batch_launches_nothing():
+    lib = gdn.load()
+    st = ctypes.c_void_p(BASE)
+    rc = lib.gdn_decode_step(ctypes.byref(D(n_seq=0, total_tokens=0)), None, None, None, None,
+                             None, None, None, None, st, None)
+    assert rc == gdn.GDN_OK
