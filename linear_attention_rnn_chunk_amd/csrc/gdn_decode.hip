@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void gdn_decode(DecodeParams p) {
   f32x4 s[RPT];
   if (p.h_in) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) s[i] = *(const f32x4*)(p.h_in + sbase + (int64_t)(r0 + 32 * i) * p.dv);
+    for (int i = 0; i < RPT; ++i)
+      s[i] = __builtin_nontemporal_load((const f32x4*)(p.h_in + sbase + (int64_t)(r0 + 32 * i) * p.dv));
   } else {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void gdn_decode(DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     s[i] += kr[i] * u;
-    *(f32x4*)(p.h_out + sbase + (int64_t)(r0 + 32 * i) * p.dv) = s[i];
+    __builtin_nontemporal_store(s[i], (f32x4*)(p.h_out + sbase + (int64_t)(r0 + 32 * i) * p.dv));
     bad_out |= nonfinite(s[i][0]) | nonfinite(s[i][1]) | nonfinite(s[i][2]) | nonfinite(s[i][3]);
     op += s[i] * qr[i];
   }
