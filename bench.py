@@ -318,6 +318,9 @@ def main():
     ap.add_argument("--config", default="hybrid")
     ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--compose", default="split", choices=["split", "fused"],
+                    help="split: prep kernel then scan (timed per kernel); fused: tile waves "
+                         "inside the scan workgroup, one kernel")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="before each timed step, write this much scratch memory (larger than "
@@ -401,15 +404,27 @@ def main():
     mk = lambda stages: gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else Tn, spec.hk,
                                          spec.hv, spec.dk, spec.dv, gate, chunk, qdt,
                                          gdn.BF16 if odt_t == torch.bfloat16 else gdn.F32, arm,
-                                         gdn.COMPOSE_SPLIT, stages)
+                                         gdn.COMPOSE_FUSED if fused else gdn.COMPOSE_SPLIT, stages)
+    fused = args.compose == "fused"
     p_prep, p_scan = mk(gdn.STAGE_PREP), mk(gdn.STAGE_SCAN)
+    p_all = mk(gdn.STAGE_ALL)
     o = torch.empty((B, Tn, spec.hv, spec.dv), dtype=odt_t, device=dev)
     hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = torch.empty(gdn.workspace_bytes(p_prep), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, gdn.workspace_bytes(p_all if fused else p_prep)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        if fused:  # one kernel (plus the chunk table of a packed batch): no stage split
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            rc = gdn.chunk_fwd_raw(p_all, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
+            if ev is not None:
+                ev[2].record(stream)
+            if rc:
+                raise gdn.GdnError(rc, "gdn_chunk_fwd")
+            return
         if ev is not None:
             ev[0].record(stream)
         rc = gdn.chunk_fwd_raw(p_prep, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
@@ -460,7 +475,8 @@ def main():
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if args.arm == "bf16" else MFMA_F32_PEAK_TFLOPS
     dom = "scan" if scan_ms >= prep_ms else "prep"
     dom_ms = scan_ms if dom == "scan" else prep_ms
-    dom_bytes = alg[dom + "_bytes"]
+    # the fused kernel moves only the layer's compulsory bytes (no tiles through HBM)
+    dom_bytes = alg["layer_bytes"] if fused else alg[dom + "_bytes"]
     achieved_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     kernel_name = "gdn_scan" if dom == "scan" else "gdn_prep"
     digest = source_digest("hybrid")
@@ -485,17 +501,18 @@ def main():
                                % (spec.name, spec.n_seq, spec.tokens // spec.n_seq, spec.hk, spec.hv,
                                   spec.dk, "per-head" if gate == gdn.GATE_HEAD else "per-key-channel",
                                   chunk, ", h0" if spec.h0 else ""),
-                   "tokens": spec.tokens, "arm": args.arm, "composition": "split"},
+                   "tokens": spec.tokens, "arm": args.arm, "composition": args.compose},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel_ms": dom_ms, "algorithmic_bytes": dom_bytes},
         "mfma": {"definition": "algorithmic flops / kernel time / dense peak",
                  "peak_tflops": peak_mfma,
-                 "prep_frac": alg["prep_flops"] / (prep_ms * 1e-3) / (peak_mfma * 1e12),
-                 "scan_frac": alg["scan_flops"] / (scan_ms * 1e-3) / (peak_mfma * 1e12),
+                 "prep_frac": (alg["prep_flops"] / (prep_ms * 1e-3) / (peak_mfma * 1e12)) if not fused else None,
+                 "scan_frac": (alg["scan_flops"] + (alg["prep_flops"] if fused else 0)) / (scan_ms * 1e-3)
+                 / (peak_mfma * 1e12),
                  "layer_frac": (alg["prep_flops"] + alg["scan_flops"]) / (ms_step * 1e-3)
                  / (peak_mfma * 1e12)},
-        "kernels_ms": {"prep": prep_ms, "scan": scan_ms},
+        "kernels_ms": {"prep": prep_ms, "scan": scan_ms} if not fused else {"scan_fused": scan_ms},
         "timing": {"headline": "median cold-cache step (%d MiB scratch written before each step)"
                                % args.flush_mib if args.flush_mib else "median warm step",
                    "min_ms": float(step_ms.min()), "warm_median_ms": warm_ms},

@@ -63,9 +63,13 @@ enum { GDN_BF16 = 0, GDN_F32 = 1 };
 /* Arithmetic arm: bf16 MFMA operands with fp32 accumulation, or fp32 MFMA
  * operands (the fp32-fold debug arm).  The state is fp32 in both. */
 enum { GDN_ARM_MFMA_BF16 = 0, GDN_ARM_FOLD_F32 = 1 };
-/* Kernel composition: split (sequence-parallel prep, then scan) or fused
- * (one kernel computes the chunk tiles and runs the scan).  AUTO picks the
- * measured default for the problem. */
+/* Kernel composition: split (a sequence-parallel prep kernel writes every chunk's T and
+ * P to the workspace, then the scan reads them) or fused (two extra waves of each scan
+ * workgroup form T and P a chunk ahead and hand them over in LDS; no tile round trip
+ * through HBM, but the tiles are formed once per 32-column slice of the state).  The
+ * two give bit-identical results.  FUSED is built for the per-head gate with bf16
+ * q/k/v on the bf16 arm (GDN_E_UNSUPPORTED otherwise) and has no separate stages.  AUTO
+ * picks the measured default: split. */
 enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2 };
 /* Stages of the split composition a call runs.  0 (or PREP|SCAN) runs both.  A
  * SCAN-only call consumes the chunk tiles a previous PREP call (same problem, same

@@ -29,8 +29,13 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   if (p->compose != GDN_COMPOSE_AUTO && p->compose != GDN_COMPOSE_SPLIT &&
       p->compose != GDN_COMPOSE_FUSED)
     return GDN_E_UNSUPPORTED;
-  if (p->compose == GDN_COMPOSE_FUSED) return GDN_E_UNSUPPORTED;  // not built yet
   if (p->stages < 0 || p->stages > (GDN_STAGE_PREP | GDN_STAGE_SCAN)) return GDN_E_UNSUPPORTED;
+  // the fused composition (tile waves inside the scan workgroup) is built for the
+  // per-head gate with bf16 inputs on the bf16 arm, and has no separate stages
+  if (p->compose == GDN_COMPOSE_FUSED &&
+      (p->gate != GDN_GATE_HEAD || p->qkv_dtype != GDN_BF16 || p->arm != GDN_ARM_MFMA_BF16 ||
+       !(p->stages == GDN_STAGE_ALL || p->stages == (GDN_STAGE_PREP | GDN_STAGE_SCAN))))
+    return GDN_E_UNSUPPORTED;
 
   Plan pl;
   memset(&pl, 0, sizeof(pl));
@@ -46,7 +51,7 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   pl.arm_f32 = p->arm == GDN_ARM_FOLD_F32;
   pl.qkv_f32 = p->qkv_dtype == GDN_F32;
   pl.o_f32 = p->o_dtype == GDN_F32;
-  pl.fused = 0;
+  pl.fused = p->compose == GDN_COMPOSE_FUSED;
   pl.run_prep = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_PREP);
   pl.run_scan = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_SCAN);
   // The fixed-length form is chosen when seq_len > 0 or when there are no tokens at all;
@@ -69,7 +74,8 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   size_t off = 0;
   pl.off_table = off;
   off = round_up(off + (pl.varlen ? 2 * sizeof(int32_t) * (size_t)(pl.n_seq + 1) : 0), 256);
-  const size_t tile = (size_t)pl.max_slots * pl.hv * gdn::tile_elems(C) * esz;
+  // split composition: T and P of every chunk pass through the workspace
+  const size_t tile = pl.fused ? 0 : (size_t)pl.max_slots * pl.hv * gdn::tile_elems(C) * esz;
   pl.off_T = off;
   off = round_up(off + tile, 256);
   pl.off_P = off;

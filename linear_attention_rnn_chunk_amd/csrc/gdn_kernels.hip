@@ -559,15 +559,167 @@ __device__ __forceinline__ typename Arm::F frag_of(const u32x4* raw) {
 }
 
 // ----------------------------------------------------------- prep -------
+// The tile work of one (chunk, value head) under the per-head gate, in pieces shared by
+// the prep kernel and the fused scan's tile waves (the same instructions on the same
+// values, so both compositions produce bit-identical T and P):
+//   tile_loads     K and Q operand fragments of the chunk straight from global memory
+//                  (rows past a partial chunk's end re-read its last row, in bounds), and
+//                  the gate and beta of row `lane`
+//   tile_products  the lower 16 x 16 tiles of K K^T and Q K^T on MFMA, oriented so the
+//                  accumulator lanes are the rows (A operand = rows of tile st, B operand
+//                  = rows of tile rt)
+//   tile_sweep     the in-chunk gate prefix G and the masked beta rows, into LDS
+// then wave_tiles forms A and P, solves for T and stores both as scan fragments.
+template <int DK, int C, bool QF32>
+struct TileRegs {
+  static constexpr int NBK = DK / 32, NT = C / 16, EPL = QF32 ? 2 : 1;  // 16-byte loads per fragment
+  u32x4 rk[NBK][NT][EPL], rq[NBK][NT][EPL];
+  float xl, bl;  // gate and beta of row min(lane, L - 1)
+};
+
+template <int DK, int C, bool QF32>
+__device__ __forceinline__ void tile_loads(const Params& p, int64_t t0, int L, int kh, int h, int lane,
+                                           TileRegs<DK, C, QF32>& R) {
+  constexpr int NT = C / 16, NBK = DK / 32, ESZ = QF32 ? 4 : 2, EPL = QF32 ? 2 : 1;
+  const int i = lane & 15, g = lane >> 4;
+  const int rg = lane < L ? lane : L - 1;
+  R.xl = p.g[(t0 + rg) * p.hv + h];
+  R.bl = p.beta[(t0 + rg) * p.hv + h];
+  const int64_t cbase = (t0 * p.hk + kh) * (int64_t)(DK * ESZ);  // chunk's first row
+  const char* kbase = (const char*)p.k + cbase;
+  const char* qbase = (const char*)p.q + cbase;
+  const uint32_t rstride = (uint32_t)(p.hk * DK * ESZ);
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const int r = 16 * rt + i;
+    const uint32_t o = (uint32_t)(r < L ? r : L - 1) * rstride + 8 * g * ESZ;
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) {
+        R.rk[kb][rt][x] = *(const u32x4*)(kbase + o + (32 * kb + 4 * x) * ESZ);
+        R.rq[kb][rt][x] = *(const u32x4*)(qbase + o + (32 * kb + 4 * x) * ESZ);
+      }
+  }
+}
+
+// Inf/NaN anywhere in the loaded K and Q fragments
+template <int DK, int C, bool QF32>
+__device__ __forceinline__ uint32_t tile_kq_nonfinite(const TileRegs<DK, C, QF32>& R) {
+  uint32_t nf = 0;
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < C / 16; ++rt)
+#pragma unroll
+      for (int x = 0; x < (QF32 ? 2 : 1); ++x) nf |= nf_bits16<QF32>(R.rk[kb][rt][x]) | nf_bits16<QF32>(R.rq[kb][rt][x]);
+  return flag_if(nf, GDN_ST_NONFINITE_INPUT);
+}
+
+template <class Arm, int DK, int C, bool QF32>
+__device__ __forceinline__ void tile_products(const TileRegs<DK, C, QF32>& R, f32x4* accA, f32x4* accP) {
+  using F = typename Arm::F;
+  constexpr int NT = C / 16, NTRI = NT * (NT + 1) / 2;
+#pragma unroll
+  for (int t = 0; t < NTRI; ++t) {
+    accA[t] = zero4();
+    accP[t] = zero4();
+  }
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb) {
+    F kf[NT], qf[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      kf[rt] = frag_of<Arm, QF32>(R.rk[kb][rt]);
+      qf[rt] = frag_of<Arm, QF32>(R.rq[kb][rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int st = 0; st <= rt; ++st) {
+        accA[tri(rt, st)] = Arm::mma(kf[st], kf[rt], accA[tri(rt, st)]);
+        accP[tri(rt, st)] = Arm::mma(kf[st], qf[rt], accP[tri(rt, st)]);
+      }
+  }
+}
+
+// tile_loads + tile_products with fewer registers live (bf16 inputs), for the fused scan's
+// tile waves: every K fragment is loaded first, the Q fragments one row tile ahead of
+// their use.  Each tile still accumulates over kb = 0, 1, ... in order with the same
+// operands, so its sums are bit-identical to tile_products'.  Returns the K/Q status bits.
+template <class Arm, int DK, int C>
+__device__ __forceinline__ uint32_t tile_products_lean(const Params& p, int64_t t0, int L, int kh, int h,
+                                                       int lane, f32x4* accA, f32x4* accP, float& xl,
+                                                       float& bl) {
+  using F = typename Arm::F;
+  constexpr int NT = C / 16, NBK = DK / 32, NTRI = NT * (NT + 1) / 2, ESZ = 2;
+  const int i = lane & 15, g = lane >> 4;
+  const int rg = lane < L ? lane : L - 1;
+  xl = p.g[(t0 + rg) * p.hv + h];
+  bl = p.beta[(t0 + rg) * p.hv + h];
+  const int64_t cbase = (t0 * p.hk + kh) * (int64_t)(DK * ESZ);
+  const char* kbase = (const char*)p.k + cbase;
+  const char* qbase = (const char*)p.q + cbase;
+  const uint32_t rstride = (uint32_t)(p.hk * DK * ESZ);
+  auto roff = [&](int rt) __attribute__((always_inline)) {
+    const int r = 16 * rt + i;
+    return (uint32_t)(r < L ? r : L - 1) * rstride + 8 * g * ESZ;
+  };
+  u32x4 rk[NBK][NT], rq[2][NBK];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb) rk[kb][rt] = *(const u32x4*)(kbase + roff(rt) + 32 * kb * ESZ);
+#pragma unroll
+  for (int kb = 0; kb < NBK; ++kb) rq[0][kb] = *(const u32x4*)(qbase + roff(0) + 32 * kb * ESZ);
+#pragma unroll
+  for (int t = 0; t < NTRI; ++t) {
+    accA[t] = zero4();
+    accP[t] = zero4();
+  }
+  uint32_t nf = 0;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    if (rt + 1 < NT) {
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb) rq[(rt + 1) & 1][kb] = *(const u32x4*)(qbase + roff(rt + 1) + 32 * kb * ESZ);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb) {
+      nf |= nf_bits16<false>(rk[kb][rt]) | nf_bits16<false>(rq[rt & 1][kb]);
+      const F kr = frag_of<Arm, false>(&rk[kb][rt]), qr = frag_of<Arm, false>(&rq[rt & 1][kb]);
+#pragma unroll
+      for (int st = 0; st <= rt; ++st) {
+        const F ks = frag_of<Arm, false>(&rk[kb][st]);
+        accA[tri(rt, st)] = Arm::mma(ks, kr, accA[tri(rt, st)]);
+        accP[tri(rt, st)] = Arm::mma(ks, qr, accP[tri(rt, st)]);
+      }
+    }
+  }
+  return flag_if(nf, GDN_ST_NONFINITE_INPUT);
+}
+
+// G (inclusive prefix of the gate) and beta of the chunk's rows into Gs, Bs (rows past
+// the end contribute gate 0 and beta 0); returns the status bits of the gate and beta
+template <int C>
+__device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int lane, float* Gs, float* Bs) {
+  const float x = lane < L ? xl : 0.f, b = lane < L ? bl : 0.f;
+  uint32_t bad = flag_if(f_nonfinite(x) | f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
+  bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
+  const float G = wave_prefix_sum(x, lane);
+  if (lane < C) {
+    Gs[lane] = G;
+    Bs[lane] = b;
+  }
+  return bad;
+}
+
 // Per-head gate: one wave per (chunk slot, value head), no barrier.  A workgroup holds up
 // to 4 value heads of one key head (blockDim = 64 * min(group, 4)), so the waves that read
-// the same K and Q rows run side by side on one CU and fetch them from HBM once.
-// The wave takes its K and Q operand fragments straight from global memory,
-// forms KK^T and (Q K^T) lower tiles on MFMA (contraction over dk in contiguous
-// 8-element pieces), runs its gate sweep, and hands the products to wave_tiles.
+// the same K and Q rows run side by side on one CU and fetch them from HBM once.  Every
+// global load is issued first, then the math.
 template <class Arm, int DK, int C, bool QF32>
 __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
-  using F = typename Arm::F;
   using SL = SolveLds<C>;
   constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32;
   const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
@@ -584,50 +736,12 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
   float* S = (float*)gdn_smem + w * SL::FLOATS;
   float* Gs = S + NTRI * kTile;
   float* Bs = Gs + C;
-  uint32_t bad = 0;
 
-  // every global load first (gate and beta, then all K and Q fragments), then the math.
-  // Rows past a partial chunk's end re-read its last row (in bounds); their beta is
-  // zero, so their A rows vanish, and P masks them at formation.
-  const int rg = lane < L ? lane : L - 1;
-  const float xl = p.g[(t0 + rg) * p.hv + h], bl = p.beta[(t0 + rg) * p.hv + h];
-  constexpr int ESZ = QF32 ? 4 : 2, EPL = QF32 ? 2 : 1;  // 16-byte loads per fragment
-  const int64_t cbase = (t0 * p.hk + kh) * (int64_t)(DK * ESZ);  // chunk's first row
-  const char* kbase = (const char*)p.k + cbase;
-  const char* qbase = (const char*)p.q + cbase;
-  const uint32_t rstride = (uint32_t)(p.hk * DK * ESZ);
-  u32x4 rk[NBK][NT][EPL], rq[NBK][NT][EPL];
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    const int r = 16 * rt + i;
-    const uint32_t o = (uint32_t)(r < L ? r : L - 1) * rstride + 8 * g * ESZ;
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-      for (int x = 0; x < EPL; ++x) {
-        rk[kb][rt][x] = *(const u32x4*)(kbase + o + (32 * kb + 4 * x) * ESZ);
-        rq[kb][rt][x] = *(const u32x4*)(qbase + o + (32 * kb + 4 * x) * ESZ);
-      }
-  }
-  {  // gate sweep and beta of row `lane`
-    const float x = lane < L ? xl : 0.f, b = lane < L ? bl : 0.f;
-    bad |= flag_if(f_nonfinite(x) | f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
-    bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
-    const float G = wave_prefix_sum(x, lane);
-    if (lane < C) {
-      Gs[lane] = G;
-      Bs[lane] = b;
-    }
-  }
+  TileRegs<DK, C, QF32> R;
+  tile_loads<DK, C, QF32>(p, t0, L, kh, h, lane, R);
+  uint32_t bad = tile_sweep<C>(R.xl, R.bl, L, lane, Gs, Bs);
   if (j == 0) {  // once per key head (wave-uniform)
-    uint32_t nf = 0;
-#pragma unroll
-    for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int x = 0; x < EPL; ++x) nf |= nf_bits16<QF32>(rk[kb][rt][x]) | nf_bits16<QF32>(rq[kb][rt][x]);
-    bad |= flag_if(nf, GDN_ST_NONFINITE_INPUT);
+    bad |= tile_kq_nonfinite<DK, C, QF32>(R);
     if (p.kq_ws) {
       // K and Q in the arm's element type, [slot][key head][C][DK], for the scan (inputs
       // in fp32, or the fp32 arm); rows past the chunk end repeat its last row
@@ -639,36 +753,13 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
           const int o = (16 * rt + i) * DK + 32 * kb + 8 * g;
-          Arm::stf(kc + o, frag_of<Arm, QF32>(rk[kb][rt]));
-          Arm::stf(qc + o, frag_of<Arm, QF32>(rq[kb][rt]));
+          Arm::stf(kc + o, frag_of<Arm, QF32>(R.rk[kb][rt]));
+          Arm::stf(qc + o, frag_of<Arm, QF32>(R.rq[kb][rt]));
         }
     }
   }
-
   f32x4 accA[NTRI], accP[NTRI];
-#pragma unroll
-  for (int t = 0; t < NTRI; ++t) {
-    accA[t] = zero4();
-    accP[t] = zero4();
-  }
-#pragma unroll
-  for (int kb = 0; kb < NBK; ++kb) {
-    F kf[NT], qf[NT];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      kf[rt] = frag_of<Arm, QF32>(rk[kb][rt]);
-      qf[rt] = frag_of<Arm, QF32>(rq[kb][rt]);
-    }
-    // tile (rt, st): A operand = rows of tile st, B operand = rows of tile rt, so the
-    // accumulator's lanes are the rows r of tile rt
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-      for (int st = 0; st <= rt; ++st) {
-        accA[tri(rt, st)] = Arm::mma(kf[st], kf[rt], accA[tri(rt, st)]);
-        accP[tri(rt, st)] = Arm::mma(kf[st], qf[rt], accP[tri(rt, st)]);
-      }
-  }
+  tile_products<Arm, DK, C, QF32>(R, accA, accP);
   typedef typename Arm::T T;
   const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
   wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
@@ -894,7 +985,7 @@ __device__ __forceinline__ typename Arm::F kt_frag(const unsigned char* K, int s
   }
 }
 
-template <class Arm, int DK, int C, bool KDA, bool QF32>
+template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED>
 struct ScanLds {
   typedef typename Arm::T T;
   static constexpr int NBK = DK / 32, NBC = C / 32;
@@ -907,51 +998,59 @@ struct ScanLds {
   static constexpr int HB = 0;
   static constexpr int RO = HB + 2 * 2 * NBK * FRAG;
   static constexpr int EXCH = RO + 2 * 2 * NBC * FRAG;
+  // fused composition: T and P of the next chunks in two slots each (slot = chunk parity),
+  // and the tile waves' shared solve scratch, after the exchange
+  static constexpr int TILEB = rnd(tile_elems(C) * (int)sizeof(T));
+  static constexpr int TT = EXCH;
+  static constexpr int TP = TT + (FUSED ? 2 * TILEB : 0);
+  static constexpr int SS = TP + (FUSED ? 2 * TILEB : 0);
+  static constexpr int FIXED = SS + (FUSED ? rnd(SolveLds<C>::FLOATS * 4) : 0);
   // one chunk buffer: K (per-channel gate: e^G K, then e^{G_C - G} K), Q (e^G Q) when it
   // fits, P fragments, 32 V columns (input type), raw gate/beta rows, row scalars.  (T
   // fragments go straight from global memory to the chain waves' registers.)
   static constexpr int NDD = KDA ? (DK + 63) / 64 : 0;  // per-channel decay copies
   static constexpr int NSC = 4 * C + (KDA ? DK : 4);    // beta, beta e^G, e^{G_C-G}, e^G, decay
   static constexpr int buf_bytes(bool qr) {
-    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(tile_elems(C) * (int)sizeof(T)) + rnd(C * 32 * ESZV) +
+    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + (FUSED ? 0 : TILEB) + rnd(C * 32 * ESZV) +
            (KDA ? 0 : 256) + 256 + NDD * 256 + rnd(NSC * 4);
   }
   // Q goes through the ring (copied like K, read from LDS by the output wave) when two
   // buffers still fit; otherwise the output wave loads its Q fragments itself
-  static constexpr bool QR = 2 * buf_bytes(true) + EXCH <= LDS_MAX;
+  static constexpr bool QR = 2 * buf_bytes(true) + FIXED <= LDS_MAX;
   static constexpr int KY = 0;
   static constexpr int KH = KY + (KDA ? OPB : 0);
   static constexpr int QO = KH + OPB;
   static constexpr int PP = QO + (QR ? OPB : 0);
-  static constexpr int VV = PP + rnd(tile_elems(C) * (int)sizeof(T));
+  static constexpr int VV = PP + (FUSED ? 0 : TILEB);  // P fragments (split composition)
   static constexpr int GX = VV + rnd(C * 32 * ESZV);  // gate rows (per-head gate)
   static constexpr int GB = GX + (KDA ? 0 : 256);     // beta rows
   static constexpr int DC = GB + 256;                 // e^{G_C} per key channel
   static constexpr int SC = DC + NDD * 256;
   static constexpr int BUF = SC + rnd(NSC * 4);
   static_assert(BUF == buf_bytes(QR), "buffer carve-up");
-  static constexpr int NBUF = 4 * BUF + EXCH <= LDS_MAX ? 4 : (3 * BUF + EXCH <= LDS_MAX ? 3 : 2);
-  static constexpr int BYTES = NBUF * BUF + EXCH;
+  static constexpr int NBUF = 4 * BUF + FIXED <= LDS_MAX ? 4 : (3 * BUF + FIXED <= LDS_MAX ? 3 : 2);
+  static constexpr int BYTES = NBUF * BUF + FIXED;
   static_assert(BYTES <= LDS_MAX, "scan LDS budget");
   // chunks the loader keeps complete ahead of the step that reads them: two with four
   // buffers (the chain then reads the next chunk's K during the current step), else one
   static constexpr int CL = NBUF == 4 ? 2 : 1;
   // loader copy instructions per chunk
   static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;
-  static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;  // P
+  static constexpr int NDT = FUSED ? 0 : tile_elems(C) * (int)sizeof(T) / 1024;  // P
   static constexpr int NDV = C * 32 * ESZV / 1024;
   static constexpr int ND = ((KDA ? 2 : 1) + (QR ? 1 : 0)) * NDK + NDT + NDV + (KDA ? 1 : 2) + NDD;
   static_assert(NDK * 1024 == OpLayout<Arm, DK>::template bytes<C>(), "K copy granularity");
-  static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "P copy granularity");
+  static_assert(FUSED || NDT * 1024 == tile_elems(C) * (int)sizeof(T), "P copy granularity");
   static_assert(NDV * 1024 == C * 32 * ESZV, "V copy granularity");
 };
 
-template <class Arm, int DK, int C, bool KDA, bool QF32>
-__global__ __launch_bounds__(256) void gdn_scan(Params p) {
+template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED>
+__global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
   using Lay = OpLayout<Arm, DK>;
-  using SL = ScanLds<Arm, DK, C, KDA, QF32>;
+  using SL = ScanLds<Arm, DK, C, KDA, QF32, FUSED>;
+  static_assert(!FUSED || (!KDA && !QF32), "fused composition: per-head gate, bf16 inputs");
   constexpr int NT = C / 16, NBC = C / 32, NTK = DK / 16, NBK = DK / 32;
   constexpr int NBUF = SL::NBUF, LA = NBUF - 1;  // loader copies LA chunks ahead
   constexpr int CL = SL::CL;                      // ... and keeps CL chunks complete ahead
@@ -959,6 +1058,10 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
   constexpr int ESZV = SL::ESZV;
   const int tid = threadIdx.x, lane = tid & 63, i = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // roles: 0, 1 chain; 2 output; 3 loader; 4, 5 tile waves (fused composition).  Waves go
+  // to the SIMDs round-robin, so in the fused workgroup the chain waves take waves 2 and 3
+  // (SIMDs of their own) and the tile waves share SIMDs with the output and loader waves.
+  const int role = FUSED ? (wave < 4 ? (wave + 2) & 3 : wave) : wave;
   const int DV = p.dv, nslice = DV / 32;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2): give
   // each XCD a contiguous range of (sequence, value head, slice) work items, so that the
@@ -1017,7 +1120,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
   };
   const int kq_ld = (KDA || p.kq_ws) ? DK : p.hk * DK;
 
-  if (wave == 3) {
+  if (role == 3) {
     // ------------------------------------------------------------- loader ----
     // Only copies to LDS are issued here, one instruction per call, so the counts in
     // the waits below are exact.
@@ -1069,9 +1172,11 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
           dma16(vsrc + (int64_t)(r < L ? r : L - 1) * hvs * DV * ESZV + c * 16, B + SL::VV + k * 1024);
         }
       }
-      const char* psrc = (const char*)p.Pws + ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
+      if constexpr (!FUSED) {
+        const char* psrc = (const char*)p.Pws + ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
 #pragma unroll
-      for (int k = 0; k < SL::NDT; ++k) dma16(psrc + (uint32_t)(k * 1024 + lane * 16), B + SL::PP + k * 1024);
+        for (int k = 0; k < SL::NDT; ++k) dma16(psrc + (uint32_t)(k * 1024 + lane * 16), B + SL::PP + k * 1024);
+      }
       // gate and beta of row min(lane, L - 1); the sweep masks rows past the end
       const int64_t e = (t0 + (lane < L ? lane : L - 1)) * hvs + h;
       if constexpr (!KDA) dma4(p.g + e, B + SL::GX);
@@ -1141,7 +1246,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       check_v(ci);
       __syncthreads();
     }
-  } else if (wave == 2) {
+  } else if (role == 2) {
     // ------------------------------------------------------------- output ----
     // P fragments, loaded one chunk ahead of their use into two register sets.  Q row
     // fragments come from the chunk's LDS buffer, or, when Q does not fit in the ring,
@@ -1172,7 +1277,7 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       }
     };
     auto load_p = [&](int ci, int set) __attribute__((always_inline)) {  // LDS -> registers
-      const T* src = (const T*)(bufp(ci) + SL::PP);
+      const T* src = FUSED ? (const T*)(exch + SL::TP + (ci & 1) * SL::TILEB) : (const T*)(bufp(ci) + SL::PP);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -1291,9 +1396,9 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       if ((nch - 1) & 1) out_p(nch - 1, 1);
       else out_p(nch - 1, 0);
     }
-  } else {
+  } else if (role < 2) {
     // -------------------------------------------------------------- chain ----
-    const int u = wave;
+    const int u = role;
     // this lane's state column inside the slice: the two chain waves own interleaved
     // quads, so the output wave holds 8 consecutive columns of a row per lane
     const int ccol = 8 * (i >> 2) + 4 * u + (i & 3);
@@ -1345,9 +1450,11 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) kf[kb][mt] = Lay::ld8(B, 16 * mt + i, 32 * kb + 8 * g);
     };
-    if (nch > 0) load_t(0, std::integral_constant<int, 0>{});
-    if (nch > 1) load_t(1, std::integral_constant<int, 1>{});
-    wait_vm<0>();
+    if constexpr (!FUSED) {
+      if (nch > 0) load_t(0, std::integral_constant<int, 0>{});
+      if (nch > 1) load_t(1, std::integral_constant<int, 1>{});
+      wait_vm<0>();
+    }
     __syncthreads();
     if (PRE && nch > 0) load_kf(0);
     auto cstep = [&](auto PAR, int ci) __attribute__((always_inline)) {
@@ -1382,12 +1489,14 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
         if constexpr (!KDA) e4[mt] = *(const float4*)(S + C + 16 * mt + 4 * g);
       }
       F tf[NBC][NT];
+      const T* tsl = (const T*)(exch + SL::TT + par * SL::TILEB);  // fused: this chunk's T slot
 #pragma unroll
       for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)
           if (32 * sb <= 16 * mt + 15) {
-            if constexpr (sizeof(T) == 2) tf[sb][mt] = __builtin_bit_cast(F, tr_[sb][mt][0]);
+            if constexpr (FUSED) tf[sb][mt] = Arm::ld8(tsl + (tile_frag_index(mt, sb) * 64 + lane) * 8);
+            else if constexpr (sizeof(T) == 2) tf[sb][mt] = __builtin_bit_cast(F, tr_[sb][mt][0]);
             else tf[sb][mt] = Arm::ld8((const T*)tr_[sb][mt]);
           }
       // e^{G_C} H_in (the state's old part), off the product chain
@@ -1469,11 +1578,13 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
       }
       // chunk ci + 2's T into this chunk's set; chunk ci + 1's (issued a step ago) must be
       // complete at the barrier, chunk ci + 2's may stay in flight
-      if (ci + 2 < nch) {
-        load_t(ci + 2, PAR);
-        wait_vm<NTL>();
-      } else {
-        wait_vm<0>();
+      if constexpr (!FUSED) {
+        if (ci + 2 < nch) {
+          load_t(ci + 2, PAR);
+          wait_vm<NTL>();
+        } else {
+          wait_vm<0>();
+        }
       }
       __syncthreads();
     };
@@ -1490,6 +1601,56 @@ __global__ __launch_bounds__(256) void gdn_scan(Params p) {
           p.hT[hbase + (int64_t)state_dim(t, g, j) * DV + col0] = H[t][j];
         }
     }
+  } else if constexpr (FUSED) {
+    // ------------------------------------------------------ tiles (fused) ----
+    // Chunk u's T and P are formed by tile wave u & 1 over two steps, with the prep
+    // kernel's code: at step u - 2 its loads and products, at step u - 1 the gate sweep,
+    // A and P, the solve, and the stores into tile slot u & 1, which the barrier ending
+    // step u - 1 publishes to the chain and output waves for step u.  In any step only one
+    // tile wave runs the second half, so the two share one solve scratch.  (Step -1 runs
+    // before the first barrier; chunk 0's two halves both fall there.)
+    constexpr int NTRI = SolveLds<C>::NTRI;
+    const int tw = role - 4;
+    float* Sv = (float*)(exch + SL::SS);
+    float* Gs = Sv + NTRI * kTile;
+    float* Bs = Gs + C;
+    f32x4 accA[NTRI], accP[NTRI];
+    float xl = 0.f, bl = 0.f;  // gate and beta row of this lane, carried from one half to the other
+    // The lane index is passed through an empty asm in each half so the compiler derives
+    // the many lane-dependent constants of the solve there, instead of keeping them live
+    // (and spilled) across the whole loop.
+    auto half_a = [&](int cu) __attribute__((always_inline)) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      bad |= tile_products_lean<Arm, DK, C>(p, chunk_t0(cu), chunk_L(cu), kh, h, ln, accA, accP, xl, bl);
+    };
+    auto half_b = [&](int cu) __attribute__((always_inline)) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int L = chunk_L(cu);
+      bad |= tile_sweep<C>(xl, bl, L, ln, Gs, Bs);
+      T* Tout = (T*)(exch + SL::TT + (cu & 1) * SL::TILEB);
+      T* Pout = (T*)(exch + SL::TP + (cu & 1) * SL::TILEB);
+      wave_tiles<Arm, C, false>(accA, accP, Sv, Gs, Bs, Tout, Pout, L, ln);
+    };
+    // every role passes nch + 1 barriers: the first one, then one per step
+    int passed = 0;
+    if (tw == 0) {  // chunk 0: both halves before the first barrier
+      if (nch > 0) {
+        half_a(0);
+        half_b(0);
+      }
+      __syncthreads();
+      ++passed;
+    }
+    for (int cu = tw == 0 ? 2 : 1; cu < nch; cu += 2) {
+      half_a(cu);  // step cu - 2
+      __syncthreads();
+      half_b(cu);  // step cu - 1
+      __syncthreads();
+      passed += 2;
+    }
+    for (; passed < nch + 1; ++passed) __syncthreads();
   }
   if (bad) atomicOr(p.status, bad);
 }
@@ -1511,7 +1672,7 @@ bool set_lds_once(Fn fn, size_t lds) {
 
 template <class Arm, int DK, int C, bool KDA, bool QF32>
 gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
-  if (pl.run_prep && pl.max_slots > 0) {
+  if (pl.run_prep && !pl.fused && pl.max_slots > 0) {
     if constexpr (KDA) {
       const size_t lds = prep_chan_lds_bytes<Arm, DK>();
       if (!set_lds_once(gdn_prep_chan<Arm, DK, QF32>, lds)) return GDN_E_LAUNCH;
@@ -1527,10 +1688,19 @@ gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   if (pl.run_scan) {
-    const size_t lds = ScanLds<Arm, DK, C, KDA, QF32>::BYTES;
-    if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32>, lds)) return GDN_E_LAUNCH;
     const int64_t blocks = (int64_t)pl.n_seq * pl.hv * (pl.dv / 32);
-    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+    if constexpr (!KDA && !QF32 && std::is_same<Arm, ArmBF16>::value) {
+      if (pl.fused) {
+        const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, true>::BYTES;
+        if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, true>, lds)) return GDN_E_LAUNCH;
+        hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32, true>), dim3((unsigned)blocks), dim3(384), lds, st, prm);
+        return hipGetLastError() == hipSuccess ? GDN_OK : GDN_E_LAUNCH;
+      }
+    }
+    if (pl.fused) return GDN_E_UNSUPPORTED;  // refused on the host already
+    const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, false>::BYTES;
+    if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, false>, lds)) return GDN_E_LAUNCH;
+    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32, false>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   return GDN_OK;
@@ -1565,7 +1735,7 @@ gdn_status run_arm(const Plan& pl, const Params& prm, hipStream_t st) {
 
 gdn_status launch(const Plan& pl, const Params& prm, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  if (pl.varlen && pl.run_prep) {
+  if (pl.varlen && (pl.run_prep || pl.fused)) {
     hipLaunchKernelGGL(gdn_chunk_table, dim3(1), dim3(256), 0, st, prm, (int)pl.chunk);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }

@@ -65,6 +65,14 @@ def P(**kw):
     (dict(qkv_dtype=3), gdn.GDN_E_UNSUPPORTED),
     (dict(arm=2), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=9), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_FUSED), gdn.GDN_OK),
+    (dict(compose=gdn.COMPOSE_FUSED, chunk=32, dk=64, dv=32), gdn.GDN_OK),
+    # the fused composition is built for the per-head gate, bf16 inputs, the bf16 arm
+    (dict(compose=gdn.COMPOSE_FUSED, gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_FUSED, qkv_dtype=gdn.F32), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_FUSED, arm=gdn.ARM_FOLD_F32), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_FUSED, stages=gdn.STAGE_PREP), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_FUSED, stages=gdn.STAGE_PREP | gdn.STAGE_SCAN), gdn.GDN_OK),
 ])
 def test_validate_refusals(kw, code):
     assert gdn.validate(P(**kw)) == code
@@ -90,6 +98,9 @@ def test_workspace_bytes_scales_with_tiles():
         # the fp32 arm also keeps K and Q in fp32 for the scan: [slot][hk][C][dk] each
         kq = 2 * s * 2 * C * 128 * 4
         assert 2 * s * hv * elems * 4 + kq <= f32 < 2 * s * hv * elems * 4 + kq + 1024
+    # fused composition: no tiles in the workspace (only the chunk table of a packed batch)
+    assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_FUSED)) == 0
+    assert 0 < gdn.workspace_bytes(P(n_seq=3, seq_len=0, compose=gdn.COMPOSE_FUSED)) <= 256
     # packed form: slots bounded by ceil(total / C) + n_seq, plus the chunk table
     pk = gdn.workspace_bytes(P(n_seq=3, seq_len=0, chunk=64))
     assert pk >= 2 * (4 + 3) * hv * 3072 * 2
