@@ -766,16 +766,20 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
   if (bad) atomicOr(p.status, bad);
 }
 
-// Per-channel gate (C = 32): one workgroup per (chunk slot, value head).  One thread per
-// key channel sweeps the gate down the chunk and forms the gated operands: for the
-// products, factors split around the middle row m so every stored factor stays below
-// e^85 (gate >= -5, C = 32; arguments clamped, masked entries dropped by select):
+// Per-channel gate (C = 32): one workgroup per (chunk slot, value head).  The gate sweep
+// and the gated operands run on all 256 threads: thread (d, part) owns key channel d and
+// the RP = C / (256 / DK) rows of its part, loads all its g, k and q elements at once,
+// and forms the in-chunk prefix G in two levels (its own rows, then the totals of the
+// earlier parts through LDS).  Factors are split around the middle row m so every stored
+// factor stays below e^85 (gate >= -5, C = 32; arguments clamped, masked entries dropped
+// by select):
 //   Kup = K e^{G - G_m},  Kdn = K e^{G_m - G},  Qup = Q e^{G - G_m}   (LDS)
 // and for the scan e^{G} K, e^{G_C - G} K, e^{G} Q and e^{G_C} (workspace).  Then wave 0
 // forms Kup Kdn^T and Qup Kdn^T on MFMA and hands them to wave_tiles.
 template <class Arm, int DK>
 constexpr size_t prep_chan_lds_bytes() {
-  return 3 * (size_t)32 * (DK + Arm::PAD) * sizeof(typename Arm::T) + SolveLds<32>::FLOATS * sizeof(float);
+  return 3 * (size_t)32 * (DK + Arm::PAD) * sizeof(typename Arm::T) + SolveLds<32>::FLOATS * sizeof(float) +
+         (256 / DK + 1) * DK * sizeof(float);
 }
 
 template <class Arm, int DK, bool QF32>
@@ -783,6 +787,7 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
   constexpr int C = 32, NT = 2, NBK = DK / 32, KP = DK + Arm::PAD;
+  constexpr int NPART = 256 / DK, RP = C / NPART;  // parts of the chunk's rows, rows per part
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int h = (int)(blockIdx.x % p.hv);
   const int64_t slot = blockIdx.x / p.hv;
@@ -796,43 +801,72 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
   float* S = (float*)(Qup + C * KP);
   float* Gs = S + SolveLds<C>::NTRI * kTile;
   float* Bs = Gs + C;
+  float* Tot = S + SolveLds<C>::FLOATS;  // [NPART][DK] row totals of each part
+  float* Gmid = Tot + NPART * DK;        // [DK] G at the middle row
   uint32_t bad = 0;
 
-  if (tid < DK) {
-    const int d = tid;
-    float G[C];
-    float acc = 0.f;
+  const int d = tid % DK, part = tid / DK, r0 = part * RP;
+  // rows r0 .. r0 + RP - 1 (past the chunk end: the last row again, masked below)
+  const float* gsrc = p.g + ((t0 * p.hv + h) * (int64_t)DK + d);
+  const int64_t gstride = (int64_t)p.hv * DK;
+  const int64_t kqoff = (t0 * p.hk + kh) * (int64_t)DK + d, kqstride = (int64_t)p.hk * DK;
+  float x[RP], kf[RP], qf[RP];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      const int rr = r < L ? r : L - 1;
-      const float xl = p.g[((t0 + rr) * p.hv + h) * (int64_t)DK + d];
-      const float x = r < L ? xl : 0.f;
-      bad |= flag_if(f_nonfinite(x), GDN_ST_NONFINITE_INPUT);
-      bad |= flag_if((x > 0.f) | (x < -5.f), GDN_ST_GATE_DOMAIN);
-      acc += x;
-      G[r] = acc;
-    }
-    const float Gm = G[C / 2];
-    const float GC = G[C - 1];
-    T* Y = (T*)p.Gws + (slot * p.hv + h) * (int64_t)(3 * C * DK) + d;
-#pragma unroll
-    for (int r = 0; r < C; ++r) {
-      const int rr = r < L ? r : L - 1;
-      const int64_t e = ((t0 + rr) * p.hk + kh) * (int64_t)DK + d;
-      const float kl = load1(p.k, e, QF32), ql = load1(p.q, e, QF32);
-      const float kf = r < L ? kl : 0.f, qf = r < L ? ql : 0.f;
-      bad |= flag_if(f_nonfinite(kf) | f_nonfinite(qf), GDN_ST_NONFINITE_INPUT);
-      const float up = nexp(fminf(G[r] - Gm, 85.f)), dn = nexp(fminf(Gm - G[r], 85.f));
-      Kup[r * KP + d] = Arm::cvt(kf * up);
-      Kdn[r * KP + d] = Arm::cvt(kf * dn);
-      Qup[r * KP + d] = Arm::cvt(qf * up);
-      const float eg = nexp(G[r]);
-      Y[(0 * C + r) * DK] = Arm::cvt(eg * kf);
-      Y[(1 * C + r) * DK] = Arm::cvt(nexp(GC - G[r]) * kf);
-      Y[(2 * C + r) * DK] = Arm::cvt(eg * qf);
-    }
-    p.Dws[(slot * p.hv + h) * (int64_t)DK + d] = nexp(GC);
+  for (int j = 0; j < RP; ++j) {
+    const int r = r0 + j, rr = r < L ? r : L - 1;
+    x[j] = gsrc[rr * gstride];
   }
+#pragma unroll
+  for (int j = 0; j < RP; ++j) {
+    const int r = r0 + j, rr = r < L ? r : L - 1;
+    kf[j] = load1(p.k, kqoff + rr * kqstride, QF32);
+    qf[j] = load1(p.q, kqoff + rr * kqstride, QF32);
+  }
+  float G[RP];
+  {
+    float acc = 0.f;
+    uint32_t nf = 0, dom = 0;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+      const bool live = r0 + j < L;
+      x[j] = live ? x[j] : 0.f;
+      kf[j] = live ? kf[j] : 0.f;
+      qf[j] = live ? qf[j] : 0.f;
+      nf |= f_nonfinite(x[j]) | f_nonfinite(kf[j]) | f_nonfinite(qf[j]);
+      dom |= (uint32_t)((x[j] > 0.f) | (x[j] < -5.f));
+      acc += x[j];
+      G[j] = acc;
+    }
+    bad |= flag_if(nf, GDN_ST_NONFINITE_INPUT) | flag_if(dom, GDN_ST_GATE_DOMAIN);
+    Tot[part * DK + d] = acc;
+  }
+  __syncthreads();
+  float off = 0.f, GC = 0.f;
+#pragma unroll
+  for (int q = 0; q < NPART; ++q) {
+    const float t = Tot[q * DK + d];
+    if (q < part) off += t;
+    GC += t;
+  }
+#pragma unroll
+  for (int j = 0; j < RP; ++j) G[j] += off;
+  if (part == (C / 2) / RP) Gmid[d] = G[(C / 2) % RP];
+  __syncthreads();
+  const float Gm = Gmid[d];
+  T* Y = (T*)p.Gws + (slot * p.hv + h) * (int64_t)(3 * C * DK) + d;
+#pragma unroll
+  for (int j = 0; j < RP; ++j) {
+    const int r = r0 + j;
+    const float up = nexp(fminf(G[j] - Gm, 85.f)), dn = nexp(fminf(Gm - G[j], 85.f));
+    Kup[r * KP + d] = Arm::cvt(kf[j] * up);
+    Kdn[r * KP + d] = Arm::cvt(kf[j] * dn);
+    Qup[r * KP + d] = Arm::cvt(qf[j] * up);
+    const float eg = nexp(G[j]);
+    Y[(0 * C + r) * DK] = Arm::cvt(eg * kf[j]);
+    Y[(1 * C + r) * DK] = Arm::cvt(nexp(GC - G[j]) * kf[j]);
+    Y[(2 * C + r) * DK] = Arm::cvt(eg * qf[j]);
+  }
+  if (part == 0) p.Dws[(slot * p.hv + h) * (int64_t)DK + d] = nexp(GC);
   __syncthreads();
   if (w == 0) {
     {
@@ -1063,19 +1097,29 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   // (SIMDs of their own) and the tile waves share SIMDs with the output and loader waves.
   const int role = FUSED ? (wave < 4 ? (wave + 2) & 3 : wave) : wave;
   const int DV = p.dv, nslice = DV / 32;
-  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2): give
-  // each XCD a contiguous range of (sequence, value head, slice) work items, so that the
-  // workgroups reading the same key head share an L2.
-  int bid;
-  {
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  With
+  // key heads a multiple of 8, XCD x = blockIdx % 8 takes key heads x, x + 8, ... of
+  // every sequence, sequence by sequence: the workgroups reading one key head share an
+  // L2, and every XCD holds an equal share of each sequence, so a long sequence of a
+  // packed batch is not piled onto a few XCDs when the grid runs in several rounds.
+  // Otherwise each XCD takes a contiguous range of (sequence, value head, slice) items.
+  int n, h, slice;
+  if (p.hk % 8 == 0) {
+    const int x = (int)blockIdx.x % 8, pos = (int)blockIdx.x / 8;
+    const int group = p.hv / p.hk, gs = group * nslice, per_n = (p.hk / 8) * gs;
+    n = pos / per_n;
+    const int r = pos % per_n, r2 = r % gs;
+    h = ((r / gs) * 8 + x) * group + r2 / nslice;
+    slice = r2 % nslice;
+  } else {
     const int nb = (int)gridDim.x, per = nb / 8, rem = nb % 8;
     const int x = (int)blockIdx.x % 8, pos = (int)blockIdx.x / 8;
-    bid = x * per + (x < rem ? x : rem) + pos;
+    int bid = x * per + (x < rem ? x : rem) + pos;
+    slice = bid % nslice;
+    bid /= nslice;
+    h = bid % p.hv;
+    n = bid / p.hv;
   }
-  const int slice = bid % nslice;
-  bid /= nslice;
-  const int h = bid % p.hv;
-  const int n = bid / p.hv;
   const int kh = h / (p.hv / p.hk);
 
   int64_t s0, s1, slot0;
