@@ -982,6 +982,14 @@ __device__ __forceinline__ void dma4(const void* src, unsigned char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
 }
 
+// The copy wave's workgroup barrier: its own LDS accesses complete, then s_barrier.
+// __syncthreads() would also wait for every copy still in flight (the compiler counts a
+// global-to-LDS copy as an LDS write under the barrier's fence), which would drain the
+// chunk copied ahead at every step; the copies a step needs are waited for explicitly.
+__device__ __forceinline__ void copy_wave_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt on outstanding vector memory operations only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14; expcnt and lgkmcnt at their maximum, i.e. not waited on).
 template <int N>
@@ -1032,49 +1040,67 @@ struct ScanLds {
   static constexpr int HB = 0;
   static constexpr int RO = HB + 2 * 2 * NBK * FRAG;
   static constexpr int EXCH = RO + 2 * 2 * NBC * FRAG;
-  // fused composition: T and P of the next chunks in two slots each (slot = chunk parity),
-  // and the tile waves' shared solve scratch, after the exchange
-  static constexpr int TILEB = rnd(tile_elems(C) * (int)sizeof(T));
-  static constexpr int TT = EXCH;
-  static constexpr int TP = TT + (FUSED ? 2 * TILEB : 0);
-  static constexpr int SS = TP + (FUSED ? 2 * TILEB : 0);
-  static constexpr int FIXED = SS + (FUSED ? rnd(SolveLds<C>::FLOATS * 4) : 0);
-  // one chunk buffer: K (per-channel gate: e^G K, then e^{G_C - G} K), Q (e^G Q) when it
-  // fits, P fragments, 32 V columns (input type), raw gate/beta rows, row scalars.  (T
-  // fragments go straight from global memory to the chain waves' registers.)
+  static constexpr int TILEB = rnd(tile_elems(C) * (int)sizeof(T));  // T or P fragments of a chunk
   static constexpr int NDD = KDA ? (DK + 63) / 64 : 0;  // per-channel decay copies
   static constexpr int NSC = 4 * C + (KDA ? DK : 4);    // beta, beta e^G, e^{G_C-G}, e^G, decay
-  static constexpr int buf_bytes(bool qr) {
-    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + (FUSED ? 0 : TILEB) + rnd(C * 32 * ESZV) +
-           (KDA ? 0 : 256) + 256 + NDD * 256 + rnd(NSC * 4);
+  static constexpr int SCB = rnd(NSC * 4);
+  static constexpr int SSB = FUSED ? rnd(SolveLds<C>::FLOATS * 4) : 0;  // fused: solve scratch
+  // A chunk buffer of the ring holds K (per-channel gate: e^G K, then e^{G_C - G} K), Q
+  // (e^G Q) when it fits, 32 V columns (input type) and the raw gate / beta rows.  Two
+  // layouts place the rest:
+  //   TL  T and P of the chunk in use and the next one in two slots each (slot = chunk
+  //       parity) and the chunk scalars in CL + 1 slots, all after the exchange.  The
+  //       loader copies T and P one chunk ahead (split), or the tile waves write them
+  //       (fused); the chain reads T from LDS and issues no global load in its loop.
+  //   !TL P and the scalars inside each ring buffer; T goes straight from global memory
+  //       to the chain waves' registers, two chunks ahead.  Used where TL would leave
+  //       fewer buffers (the fp32 arm at dk = 128).
+  static constexpr int base_bytes(bool qr) {
+    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * 32 * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256;
   }
+  static constexpr int FIXA = EXCH + 4 * TILEB + SSB;
+  static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX;
+  static constexpr int BUFA = base_bytes(QRA);
+  static constexpr int NBUFA = 4 * BUFA + FIXA + 3 * SCB <= LDS_MAX ? 4
+                               : (3 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 3 : (2 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 2 : 0));
+  static constexpr bool QRB = 2 * (base_bytes(true) + TILEB + SCB) + EXCH <= LDS_MAX;
+  static constexpr int BUFB = base_bytes(QRB) + TILEB + SCB;
+  static constexpr int NBUFB = 4 * BUFB + EXCH <= LDS_MAX ? 4 : (3 * BUFB + EXCH <= LDS_MAX ? 3 : 2);
+  static constexpr bool TL = FUSED || (NBUFA >= 2 && NBUFA >= NBUFB && (QRA || !QRB));
   // Q goes through the ring (copied like K, read from LDS by the output wave) when two
   // buffers still fit; otherwise the output wave loads its Q fragments itself
-  static constexpr bool QR = 2 * buf_bytes(true) + FIXED <= LDS_MAX;
-  static constexpr int KY = 0;
-  static constexpr int KH = KY + (KDA ? OPB : 0);
-  static constexpr int QO = KH + OPB;
-  static constexpr int PP = QO + (QR ? OPB : 0);
-  static constexpr int VV = PP + (FUSED ? 0 : TILEB);  // P fragments (split composition)
-  static constexpr int GX = VV + rnd(C * 32 * ESZV);  // gate rows (per-head gate)
-  static constexpr int GB = GX + (KDA ? 0 : 256);     // beta rows
-  static constexpr int DC = GB + 256;                 // e^{G_C} per key channel
-  static constexpr int SC = DC + NDD * 256;
-  static constexpr int BUF = SC + rnd(NSC * 4);
-  static_assert(BUF == buf_bytes(QR), "buffer carve-up");
-  static constexpr int NBUF = 4 * BUF + FIXED <= LDS_MAX ? 4 : (3 * BUF + FIXED <= LDS_MAX ? 3 : 2);
-  static constexpr int BYTES = NBUF * BUF + FIXED;
-  static_assert(BYTES <= LDS_MAX, "scan LDS budget");
+  static constexpr bool QR = TL ? QRA : QRB;
+  static constexpr int NBUF = TL ? NBUFA : NBUFB;
   // chunks the loader keeps complete ahead of the step that reads them: two with four
   // buffers (the chain then reads the next chunk's K during the current step), else one
   static constexpr int CL = NBUF == 4 ? 2 : 1;
+  static constexpr int NSCS = CL + 1;  // TL: scalar slots (chunks ci .. ci + CL)
+  static constexpr int KY = 0;
+  static constexpr int KH = KY + (KDA ? OPB : 0);
+  static constexpr int QO = KH + OPB;
+  static constexpr int PP = QO + (QR ? OPB : 0);      // !TL: P fragments
+  static constexpr int VV = PP + (TL ? 0 : TILEB);
+  static constexpr int GX = VV + rnd(C * 32 * ESZV);  // gate rows (per-head gate)
+  static constexpr int GB = GX + (KDA ? 0 : 256);     // beta rows
+  static constexpr int DC = GB + 256;                 // e^{G_C} per key channel
+  static constexpr int SC = DC + NDD * 256;           // !TL: row scalars
+  static constexpr int BUF = SC + (TL ? 0 : SCB);
+  static_assert(BUF == (TL ? BUFA : BUFB), "buffer carve-up");
+  // after the exchange (TL): T slots, P slots, scalar slots, then the fused solve scratch
+  static constexpr int TT = EXCH;
+  static constexpr int TP = TT + 2 * TILEB;
+  static constexpr int SCR = TP + 2 * TILEB;
+  static constexpr int SS = SCR + NSCS * SCB;
+  static constexpr int FIXED = TL ? SS + SSB : EXCH;
+  static constexpr int BYTES = NBUF * BUF + FIXED;
+  static_assert(NBUF >= 2 && BYTES <= LDS_MAX, "scan LDS budget");
   // loader copy instructions per chunk
   static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;
-  static constexpr int NDT = FUSED ? 0 : tile_elems(C) * (int)sizeof(T) / 1024;  // P
+  static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;  // T or P of a chunk
   static constexpr int NDV = C * 32 * ESZV / 1024;
-  static constexpr int ND = ((KDA ? 2 : 1) + (QR ? 1 : 0)) * NDK + NDT + NDV + (KDA ? 1 : 2) + NDD;
+  static constexpr int ND = ((KDA ? 2 : 1) + (QR ? 1 : 0)) * NDK + (TL ? 0 : NDT) + NDV + (KDA ? 1 : 2) + NDD;
   static_assert(NDK * 1024 == OpLayout<Arm, DK>::template bytes<C>(), "K copy granularity");
-  static_assert(FUSED || NDT * 1024 == tile_elems(C) * (int)sizeof(T), "P copy granularity");
+  static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "T / P copy granularity");
   static_assert(NDV * 1024 == C * 32 * ESZV, "V copy granularity");
 };
 
@@ -1138,7 +1164,10 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   unsigned char* const ring = gdn_smem;
   unsigned char* const exch = gdn_smem + NBUF * SL::BUF;
   auto bufp = [&](int ci) __attribute__((always_inline)) { return ring + (ci % NBUF) * SL::BUF; };
-  auto scal = [&](int ci) __attribute__((always_inline)) { return (float*)(bufp(ci) + SL::SC); };
+  auto scal = [&](int ci) __attribute__((always_inline)) {
+    if constexpr (SL::TL) return (float*)(exch + SL::SCR + (ci % SL::NSCS) * SL::SCB);
+    else return (float*)(bufp(ci) + SL::SC);
+  };
   auto hb_at = [&](int par, int u, int kb) __attribute__((always_inline)) {
     return (T*)(exch + SL::HB + ((par * 2 + u) * NBK + kb) * SL::FRAG) + lane * 8;
   };
@@ -1216,7 +1245,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           dma16(vsrc + (int64_t)(r < L ? r : L - 1) * hvs * DV * ESZV + c * 16, B + SL::VV + k * 1024);
         }
       }
-      if constexpr (!FUSED) {
+      if constexpr (!SL::TL) {
         const char* psrc = (const char*)p.Pws + ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
 #pragma unroll
         for (int k = 0; k < SL::NDT; ++k) dma16(psrc + (uint32_t)(k * 1024 + lane * 16), B + SL::PP + k * 1024);
@@ -1229,6 +1258,20 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         const float* D = p.Dws + ((slot0 + ci) * hvs + h) * (int64_t)DK;
 #pragma unroll
         for (int m = 0; m < SL::NDD; ++m) dma4(D + min(lane + 64 * m, DK - 1), B + SL::DC + m * 256);
+      }
+    };
+    // TL, split composition: T and P of chunk ci into their slots (ci & 1)
+    auto issue_tp = [&](int ci) __attribute__((always_inline)) {
+      if constexpr (SL::TL && !FUSED) {
+        const int64_t tofs = ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
+        const char* tsrc = (const char*)p.Tws + tofs;
+        const char* psrc = (const char*)p.Pws + tofs;
+        unsigned char* td = exch + SL::TT + (ci & 1) * SL::TILEB;
+        unsigned char* pd = exch + SL::TP + (ci & 1) * SL::TILEB;
+#pragma unroll
+        for (int k = 0; k < SL::NDT; ++k) dma16(tsrc + (uint32_t)(k * 1024 + lane * 16), td + k * 1024);
+#pragma unroll
+        for (int k = 0; k < SL::NDT; ++k) dma16(psrc + (uint32_t)(k * 1024 + lane * 16), pd + k * 1024);
       }
     };
     auto sweep = [&](int ci) __attribute__((always_inline)) {  // scalars of chunk ci
@@ -1271,6 +1314,9 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // one chunk's copies (LA - CL <= 1) may stay in flight past a wait, so each wait
     // allows either ND outstanding copies (when a later chunk was issued) or none.
     static_assert(LA - CL <= 1, "one chunk in flight beyond the completed window");
+    // (TL, split: T and P of chunk c are issued before the copies of chunk c + LA, so the
+    // same waits complete them a step ahead of their use)
+    if (nch > 0) issue_tp(0);
 #pragma unroll
     for (int j = 0; j < LA; ++j)
       if (j < nch) issue(j);
@@ -1279,16 +1325,18 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
 #pragma unroll
     for (int j = 0; j < CL; ++j)
       if (j < nch) sweep(j);
-    __syncthreads();
+    copy_wave_barrier();
     for (int ci = 0; ci < nch; ++ci) {
       const bool more = ci + LA < nch;
+      if (ci + 1 < nch) issue_tp(ci + 1);
       if (more) issue(ci + LA);
-      // chunk ci + CL complete: all copies but this step's
+      // chunk ci + CL complete: all copies but this step's, which stay in flight across
+      // the barrier
       if (LA > CL && more) wait_vm<(LA > CL ? SL::ND : 0)>();
       else wait_vm<0>();
       if (ci + CL < nch) sweep(ci + CL);
       check_v(ci);
-      __syncthreads();
+      copy_wave_barrier();
     }
   } else if (role == 2) {
     // ------------------------------------------------------------- output ----
@@ -1321,7 +1369,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       }
     };
     auto load_p = [&](int ci, int set) __attribute__((always_inline)) {  // LDS -> registers
-      const T* src = FUSED ? (const T*)(exch + SL::TP + (ci & 1) * SL::TILEB) : (const T*)(bufp(ci) + SL::PP);
+      const T* src = SL::TL ? (const T*)(exch + SL::TP + (ci & 1) * SL::TILEB) : (const T*)(bufp(ci) + SL::PP);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -1494,7 +1542,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) kf[kb][mt] = Lay::ld8(B, 16 * mt + i, 32 * kb + 8 * g);
     };
-    if constexpr (!FUSED) {
+    if constexpr (!SL::TL) {
       if (nch > 0) load_t(0, std::integral_constant<int, 0>{});
       if (nch > 1) load_t(1, std::integral_constant<int, 1>{});
       wait_vm<0>();
@@ -1533,13 +1581,13 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         if constexpr (!KDA) e4[mt] = *(const float4*)(S + C + 16 * mt + 4 * g);
       }
       F tf[NBC][NT];
-      const T* tsl = (const T*)(exch + SL::TT + par * SL::TILEB);  // fused: this chunk's T slot
+      const T* tsl = (const T*)(exch + SL::TT + par * SL::TILEB);  // TL: this chunk's T slot
 #pragma unroll
       for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)
           if (32 * sb <= 16 * mt + 15) {
-            if constexpr (FUSED) tf[sb][mt] = Arm::ld8(tsl + (tile_frag_index(mt, sb) * 64 + lane) * 8);
+            if constexpr (SL::TL) tf[sb][mt] = Arm::ld8(tsl + (tile_frag_index(mt, sb) * 64 + lane) * 8);
             else if constexpr (sizeof(T) == 2) tf[sb][mt] = __builtin_bit_cast(F, tr_[sb][mt][0]);
             else tf[sb][mt] = Arm::ld8((const T*)tr_[sb][mt]);
           }
@@ -1622,7 +1670,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       }
       // chunk ci + 2's T into this chunk's set; chunk ci + 1's (issued a step ago) must be
       // complete at the barrier, chunk ci + 2's may stay in flight
-      if constexpr (!FUSED) {
+      if constexpr (!SL::TL) {
         if (ci + 2 < nch) {
           load_t(ci + 2, PAR);
           wait_vm<NTL>();
