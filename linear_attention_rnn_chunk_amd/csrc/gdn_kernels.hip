@@ -1059,7 +1059,11 @@ struct ScanLds {
     return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * 32 * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256;
   }
   static constexpr int FIXA = EXCH + 4 * TILEB + SSB;
-  static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX;
+  // Q in the ring unless that costs the fourth buffer (with four, the chain prefetches
+  // the next chunk's K; the output wave then loads Q itself)
+  static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX &&
+                              !(4 * base_bytes(true) + FIXA + 3 * SCB > LDS_MAX &&
+                                4 * base_bytes(false) + FIXA + 3 * SCB <= LDS_MAX);
   static constexpr int BUFA = base_bytes(QRA);
   static constexpr int NBUFA = 4 * BUFA + FIXA + 3 * SCB <= LDS_MAX ? 4
                                : (3 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 3 : (2 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 2 : 0));
