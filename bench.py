@@ -153,6 +153,89 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds, label="hybrid",
 
 PROBE_MIB = 256
 
+# one rocprofv3 --pmc pass (6 SQ counters, 1 GRBM counter: within one pass's limits)
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+N_CU = 256
+
+
+def summarize_counters(pmc_dir, kt_dir, cmd, title):
+    """Per-kernel MFMA and occupancy counters from one rocprofv3 --pmc pass of this script,
+    with kernel durations from the kernel-trace run: executed MFMA flops (512 per bf16
+    MOP) per launch and their rate, MFMA busy share (busy cycles over the per-XCD active
+    cycles x CUs x 4 SIMDs), waves per launch and LDS bank conflicts per launch."""
+    import csv
+    import glob
+    import numpy as np
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def short(name):
+        m = re.search(r"(gdn_\w+)<", name) or re.search(r"(gdn_\w+)\(", name)
+        return m.group(1) if m else None
+
+    per = {}
+    for r in rows(pmc_dir, "*counter_collection.csv"):
+        k = short(r["Kernel_Name"])
+        if k:
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[k][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    dur = {}
+    for r in rows(kt_dir, "*kernel_stats.csv"):
+        k = short(r["Name"])
+        if k:
+            dur[k] = float(r["AverageNs"]) * 1e-9
+    lines = ["# rocprofv3 MFMA and occupancy counters per launch: " + title, "# command: " + cmd,
+             "# executed flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (masked triangle halves and "
+             "per-slice redundancy included: not algorithmic)",
+             "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x %d CUs x 4 SIMDs); "
+             "GRBM_GUI_ACTIVE reads the active cycles summed over the 8 XCDs" % N_CU,
+             "source_digest: %s" % source_digest("hybrid")]
+    for k in sorted(per):
+        c = {n: float(np.mean(list(v.values()))) for n, v in per[k].items()}
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        flops = mops * 512
+        lines.append("%s mfma_mops_bf16: %.6g" % (k, mops))
+        lines.append("%s executed_flops: %.6g" % (k, flops))
+        if k in dur:
+            lines.append("%s executed_tflops: %.4g (kernel %.1f us)" % (k, flops / dur[k] / 1e12, dur[k] * 1e6))
+        if c.get("GRBM_GUI_ACTIVE"):
+            lines.append("%s mfma_busy: %.4f" % (k, c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+                                                  / (c["GRBM_GUI_ACTIVE"] / 8 * N_CU * 4)))
+        for n in ("SQ_WAVES", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"):
+            if n in c:
+                lines.append("%s %s: %.6g" % (k, n, c[n]))
+    return "\n".join(lines) + "\n"
+
+
+def measured_peaks(dev):
+    """HBM copy rate (1 GiB read + 1 GiB written) and a large bf16 GEMM's rate, measured
+    here for context beside the spec peaks."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    out = {}
+    for name, fn, work in (("hbm_copy_GBps", lambda: dst.copy_(src), 2 * n * 4 / 1e9),
+                           ("bf16_gemm_8192_TFLOPs", lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = work * 10 / (e0.elapsed_time(e1) * 1e-3)
+    return out
+
 
 def cpu_baseline(inp, budget_s):
     """Oracle on the first N tokens of every value head (N calibrated to ~budget_s)."""
@@ -328,6 +411,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of this script and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
+                    help="write the MFMA / occupancy counter summary to profiles/ and exit")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also measure an HBM copy and a large bf16 GEMM (context for the rooflines)")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="time the one-token recurrent step instead: B sequences of the hybrid "
                          "layer's heads, each continuing from its own state; prints its own line")
@@ -335,6 +422,16 @@ def main():
                     help="after the timed steps, run a plain device copy of MIB MiB three times "
                          "(reads and writes MIB MiB each): the reference for scaling HBM counters")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        cmd = ("cd /tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " -d <out>/prof_mfma -o m -f csv -- "
+               "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu")
+        txt = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cmd,
+                                 "hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)")
+        with open(os.path.join(ROOT, "profiles", "mfma_counters_hybrid.txt"), "w") as f:
+            f.write(txt)
+        print(txt)
+        return
 
     if args.summarize_profiles:
         label = "decode" if args.decode else "hybrid"
@@ -521,6 +618,8 @@ def main():
     }
     if args.copy_probe:
         rec["copy_probe_bytes"] = copy_probe(args.copy_probe, dev)
+    if args.peaks:
+        rec["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu:
         log("timing the oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
