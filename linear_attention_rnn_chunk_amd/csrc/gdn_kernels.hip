@@ -1048,29 +1048,26 @@ struct ScanLds {
   // A chunk buffer of the ring holds K (per-channel gate: e^G K, then e^{G_C - G} K), Q
   // (e^G Q) when it fits, 32 V columns (input type) and the raw gate / beta rows.  Two
   // layouts place the rest:
-  //   TL  T and P of the chunk in use and the next one in two slots each (slot = chunk
-  //       parity) and the chunk scalars in CL + 1 slots, all after the exchange.  The
-  //       loader copies T and P one chunk ahead (split), or the tile waves write them
-  //       (fused); the chain reads T from LDS and issues no global load in its loop.
-  //   !TL P and the scalars inside each ring buffer; T goes straight from global memory
-  //       to the chain waves' registers, two chunks ahead.  Used where TL would leave
-  //       fewer buffers (the fp32 arm at dk = 128).
+  //   split (!TL)  P and the chunk scalars inside each ring buffer; T goes straight from
+  //       global memory to the chain waves' registers, two chunks ahead
+  //   fused (TL)   T and P of the chunk in use and the next one in two slots each (slot =
+  //       chunk parity), which the tile waves write, and the chunk scalars in CL + 1
+  //       slots, all after the exchange
+  // (Measured for the split scan at dk = 128, C = 64: the slot layout with the copy wave
+  // moving T and P is 1.5 % slower; giving up Q in the ring for a fourth buffer, 17 %.)
   static constexpr int base_bytes(bool qr) {
     return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * 32 * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256;
   }
   static constexpr int FIXA = EXCH + 4 * TILEB + SSB;
-  // Q in the ring unless that costs the fourth buffer (with four, the chain prefetches
-  // the next chunk's K; the output wave then loads Q itself)
-  static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX &&
-                              !(4 * base_bytes(true) + FIXA + 3 * SCB > LDS_MAX &&
-                                4 * base_bytes(false) + FIXA + 3 * SCB <= LDS_MAX);
+  static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX;
   static constexpr int BUFA = base_bytes(QRA);
   static constexpr int NBUFA = 4 * BUFA + FIXA + 3 * SCB <= LDS_MAX ? 4
                                : (3 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 3 : (2 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 2 : 0));
   static constexpr bool QRB = 2 * (base_bytes(true) + TILEB + SCB) + EXCH <= LDS_MAX;
   static constexpr int BUFB = base_bytes(QRB) + TILEB + SCB;
   static constexpr int NBUFB = 4 * BUFB + EXCH <= LDS_MAX ? 4 : (3 * BUFB + EXCH <= LDS_MAX ? 3 : 2);
-  static constexpr bool TL = FUSED || (NBUFA >= 2 && NBUFA >= NBUFB && (QRA || !QRB));
+  static constexpr bool TL = FUSED;
+  static_assert(!FUSED || NBUFA >= 2, "fused scan LDS budget");
   // Q goes through the ring (copied like K, read from LDS by the output wave) when two
   // buffers still fit; otherwise the output wave loads its Q fragments itself
   static constexpr bool QR = TL ? QRA : QRB;
@@ -1264,20 +1261,6 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int m = 0; m < SL::NDD; ++m) dma4(D + min(lane + 64 * m, DK - 1), B + SL::DC + m * 256);
       }
     };
-    // TL, split composition: T and P of chunk ci into their slots (ci & 1)
-    auto issue_tp = [&](int ci) __attribute__((always_inline)) {
-      if constexpr (SL::TL && !FUSED) {
-        const int64_t tofs = ((slot0 + ci) * hvs + h) * (int64_t)(tile_elems(C) * sizeof(T));
-        const char* tsrc = (const char*)p.Tws + tofs;
-        const char* psrc = (const char*)p.Pws + tofs;
-        unsigned char* td = exch + SL::TT + (ci & 1) * SL::TILEB;
-        unsigned char* pd = exch + SL::TP + (ci & 1) * SL::TILEB;
-#pragma unroll
-        for (int k = 0; k < SL::NDT; ++k) dma16(tsrc + (uint32_t)(k * 1024 + lane * 16), td + k * 1024);
-#pragma unroll
-        for (int k = 0; k < SL::NDT; ++k) dma16(psrc + (uint32_t)(k * 1024 + lane * 16), pd + k * 1024);
-      }
-    };
     auto sweep = [&](int ci) __attribute__((always_inline)) {  // scalars of chunk ci
       const unsigned char* B = bufp(ci);
       float* S = scal(ci);
@@ -1318,9 +1301,6 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // one chunk's copies (LA - CL <= 1) may stay in flight past a wait, so each wait
     // allows either ND outstanding copies (when a later chunk was issued) or none.
     static_assert(LA - CL <= 1, "one chunk in flight beyond the completed window");
-    // (TL, split: T and P of chunk c are issued before the copies of chunk c + LA, so the
-    // same waits complete them a step ahead of their use)
-    if (nch > 0) issue_tp(0);
 #pragma unroll
     for (int j = 0; j < LA; ++j)
       if (j < nch) issue(j);
@@ -1332,7 +1312,6 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     copy_wave_barrier();
     for (int ci = 0; ci < nch; ++ci) {
       const bool more = ci + LA < nch;
-      if (ci + 1 < nch) issue_tp(ci + 1);
       if (more) issue(ci + LA);
       // chunk ci + CL complete: all copies but this step's, which stay in flight across
       // the barrier
