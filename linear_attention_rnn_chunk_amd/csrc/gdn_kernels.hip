@@ -1500,8 +1500,13 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     }
     F kf[NBK][NT];  // K row fragments of the chunk being processed
     // T fragments: straight from global memory (stored in exactly this layout), two chunks
-    // ahead into two register sets (set = chunk parity); the chain issues no other global
-    // memory operation in its loop, so each step's wait leaves just the newest set in flight
+    // ahead into two register sets (set = chunk parity).  The loads are issued as inline
+    // asm, which the compiler does not track: its own waits for them are conservative
+    // across the loop back edge and would also wait for the set issued just before the
+    // barrier.  Instead each step ends with an explicit wait that leaves only the newest set
+    // in flight, and passes the completed set through an empty asm so that no use of it
+    // can be scheduled above that wait.  The chain wave issues no other global memory
+    // operation in its loop, so the counts are exact.
     constexpr int EPL = 8 / (16 / (int)sizeof(T));
     constexpr int NTL = tile_frags(C) * EPL;  // T loads per chunk (lower fragments only)
     u32x4 trs[2][NBC][NT][EPL];
@@ -1514,8 +1519,21 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int mt = 0; mt < NT; ++mt)
           if (32 * sb <= 16 * mt + 15) {
 #pragma unroll
-            for (int x = 0; x < EPL; ++x)
-              tr_[sb][mt][x] = *(const u32x4*)(src + (tile_frag_index(mt, sb) * 64 + lane) * 8 + x * (16 / (int)sizeof(T)));
+            for (int x = 0; x < EPL; ++x) {
+              const T* a = src + (tile_frag_index(mt, sb) * 64 + lane) * 8 + x * (16 / (int)sizeof(T));
+              asm volatile("global_load_dwordx4 %0, %1, off" : "=&v"(tr_[sb][mt][x]) : "v"(a));
+            }
+          }
+    };
+    auto t_done = [&](auto SET) __attribute__((always_inline)) {  // after the wait for SET
+      auto& tr_ = trs[decltype(SET)::value];
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+          if (32 * sb <= 16 * mt + 15) {
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) asm volatile("" : "+v"(tr_[sb][mt][x]));
           }
     };
     auto load_kf = [&](int ci) __attribute__((always_inline)) {
@@ -1529,6 +1547,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       if (nch > 0) load_t(0, std::integral_constant<int, 0>{});
       if (nch > 1) load_t(1, std::integral_constant<int, 1>{});
       wait_vm<0>();
+      t_done(std::integral_constant<int, 0>{});
+      t_done(std::integral_constant<int, 1>{});
     }
     __syncthreads();
     if (PRE && nch > 0) load_kf(0);
@@ -1539,15 +1559,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       const float* S = scal(ci);
       const int par = ci & 1;
       if (!PRE) load_kf(ci);
-      // Y = K H_in
-      f32x4 Y[NT];
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) Y[mt] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NBK; ++kb)
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
-      // operands of the rest of this chunk, read while the products run
+      // operands of the rest of this chunk, read (after K) while the products run
       float vv[NT][4];
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
@@ -1574,6 +1586,14 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
             else if constexpr (sizeof(T) == 2) tf[sb][mt] = __builtin_bit_cast(F, tr_[sb][mt][0]);
             else tf[sb][mt] = Arm::ld8((const T*)tr_[sb][mt]);
           }
+      // Y = K H_in
+      f32x4 Y[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) Y[mt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
       // e^{G_C} H_in (the state's old part), off the product chain
 #pragma unroll
       for (int t = 0; t < NTK; ++t) {
@@ -1660,6 +1680,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         } else {
           wait_vm<0>();
         }
+        t_done(std::integral_constant<int, cur ^ 1>{});
       }
       __syncthreads();
     };
