@@ -1500,13 +1500,10 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     }
     F kf[NBK][NT];  // K row fragments of the chunk being processed
     // T fragments: straight from global memory (stored in exactly this layout), two chunks
-    // ahead into two register sets (set = chunk parity).  The loads are issued as inline
-    // asm, which the compiler does not track: its own waits for them are conservative
-    // across the loop back edge and would also wait for the set issued just before the
-    // barrier.  Instead each step ends with an explicit wait that leaves only the newest set
-    // in flight, and passes the completed set through an empty asm so that no use of it
-    // can be scheduled above that wait.  The chain wave issues no other global memory
-    // operation in its loop, so the counts are exact.
+    // ahead into two register sets (set = chunk parity); the chain issues no other global
+    // memory operation in its loop, so each step's wait leaves just the newest set in flight.
+    // (The loads stay visible to the compiler: a load it cannot see may have its
+    // destination registers moved or reused while the data is still in flight.)
     constexpr int EPL = 8 / (16 / (int)sizeof(T));
     constexpr int NTL = tile_frags(C) * EPL;  // T loads per chunk (lower fragments only)
     u32x4 trs[2][NBC][NT][EPL];
@@ -1519,21 +1516,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int mt = 0; mt < NT; ++mt)
           if (32 * sb <= 16 * mt + 15) {
 #pragma unroll
-            for (int x = 0; x < EPL; ++x) {
-              const T* a = src + (tile_frag_index(mt, sb) * 64 + lane) * 8 + x * (16 / (int)sizeof(T));
-              asm volatile("global_load_dwordx4 %0, %1, off" : "=&v"(tr_[sb][mt][x]) : "v"(a));
-            }
-          }
-    };
-    auto t_done = [&](auto SET) __attribute__((always_inline)) {  // after the wait for SET
-      auto& tr_ = trs[decltype(SET)::value];
-#pragma unroll
-      for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt)
-          if (32 * sb <= 16 * mt + 15) {
-#pragma unroll
-            for (int x = 0; x < EPL; ++x) asm volatile("" : "+v"(tr_[sb][mt][x]));
+            for (int x = 0; x < EPL; ++x)
+              tr_[sb][mt][x] = *(const u32x4*)(src + (tile_frag_index(mt, sb) * 64 + lane) * 8 + x * (16 / (int)sizeof(T)));
           }
     };
     auto load_kf = [&](int ci) __attribute__((always_inline)) {
@@ -1547,8 +1531,6 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       if (nch > 0) load_t(0, std::integral_constant<int, 0>{});
       if (nch > 1) load_t(1, std::integral_constant<int, 1>{});
       wait_vm<0>();
-      t_done(std::integral_constant<int, 0>{});
-      t_done(std::integral_constant<int, 1>{});
     }
     __syncthreads();
     if (PRE && nch > 0) load_kf(0);
@@ -1594,6 +1576,12 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
+      // transposed K fragments for the state update, read while the products run
+      F ktf[NBC][NTK];
+#pragma unroll
+      for (int sb = 0; sb < NBC; ++sb)
+#pragma unroll
+        for (int t = 0; t < NTK; ++t) ktf[sb][t] = kt_frag<Arm, DK>(B + SL::KH, sb, t, lane);
       // e^{G_C} H_in (the state's old part), off the product chain
 #pragma unroll
       for (int t = 0; t < NTK; ++t) {
@@ -1637,12 +1625,6 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int mt = 0; mt < NT; ++mt)
           if (32 * sb <= 16 * mt + 15) R[mt] = Arm::mma(tf[sb][mt], XB[sb], R[mt]);
       __builtin_amdgcn_sched_barrier(0);
-      // transposed K fragments for the state update
-      F ktf[NBC][NTK];
-#pragma unroll
-      for (int sb = 0; sb < NBC; ++sb)
-#pragma unroll
-        for (int t = 0; t < NTK; ++t) ktf[sb][t] = kt_frag<Arm, DK>(B + SL::KH, sb, t, lane);
       // R for the output wave; e^{G_C - G} R for the state update (per-channel gate: the
       // factor is inside Ktil)
       F RS[NBC];
@@ -1680,7 +1662,6 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         } else {
           wait_vm<0>();
         }
-        t_done(std::integral_constant<int, cur ^ 1>{});
       }
       __syncthreads();
     };
