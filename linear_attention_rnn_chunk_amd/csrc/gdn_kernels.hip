@@ -725,9 +725,16 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
   const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
   const int group = p.hv / p.hk, wpb = blockDim.x >> 6, nblk = (group + wpb - 1) / wpb;
-  const int jb = blockIdx.x % nblk;
-  const int kh = (blockIdx.x / nblk) % p.hk;
-  const int64_t slot = blockIdx.x / (nblk * p.hk);
+  // Workgroups go to the 8 XCDs round-robin: XCD x = blockIdx % 8 takes the chunk slots
+  // x, x + 8, ..., all key heads of a slot together, so the gate and beta rows of a chunk
+  // (every head's values of a token share a cache line) are fetched into one L2 only.
+  // The grid is padded to whole groups of 8 slots; workgroups past the last slot exit.
+  const int ipp = p.hk * nblk;  // workgroups per slot
+  const int64_t pos = blockIdx.x / 8;
+  const int r = (int)(pos % ipp);
+  const int jb = r % nblk;
+  const int kh = r / nblk;
+  const int64_t slot = (pos / ipp) * 8 + blockIdx.x % 8;
   const int j = jb * wpb + w;  // value head inside the key head's group
   int n, L;
   int64_t t0;
@@ -1759,7 +1766,7 @@ gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
       const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
       const size_t lds = wpb * SolveLds<C>::FLOATS * sizeof(float);
       if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
-      const int64_t blocks = pl.max_slots * pl.hk * nblk;
+      const int64_t blocks = (pl.max_slots + 7) / 8 * 8 * pl.hk * nblk;  // whole groups of 8 slots
       hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)blocks), dim3(64 * wpb), lds, st, prm);
     }
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
