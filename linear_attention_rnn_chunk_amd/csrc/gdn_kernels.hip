@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "gdn_internal.h"
@@ -1740,17 +1741,20 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
 }
 
 // ------------------------------------------------------------ launch -----
-// Kernel attributes are set once per instantiation (the first launch); later launches
-// reuse them.
+// Kernel attributes are set once per instantiation and device (the first launch there);
+// later launches reuse them.
 template <class Fn>
 bool set_lds_once(Fn fn, size_t lds) {
-  static bool done = false;
-  if (!done) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-        hipSuccess)
-      return false;
-    done = true;
-  }
+  // one flag per device (the attribute belongs to the function on the current device);
+  // concurrent first calls may both set it, which is harmless
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return true;
+  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return false;
+  done.fetch_or(bit, std::memory_order_release);
   return true;
 }
 
