@@ -918,14 +918,16 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
 // Serial part: one workgroup per (sequence, value head, 32 state columns), 4 waves:
 //   waves 0, 1  chain: each owns 16 state columns; runs only the recurrence
 //               Y = K H, X = beta V - beta e^G Y, R = T X, H <- e^{G_C} H + Ktil^T R
-//               with its fp32 state in MFMA accumulators
+//               with its fp32 state in MFMA accumulators; T fragments come straight
+//               from global memory into registers, two chunks ahead
 //   wave 2      output, one chunk behind the chain: O = e^G (Q H_in) + P R for all 32
-//               columns, from H_in and R the chain waves leave in LDS and Q, P from the
-//               chunk buffer; it issues no global loads, only the O stores
-//   wave 3      loader: copies K, Q, P and V of chunk ci + NBUF - 1 global -> LDS directly
-//               (no register round trip) into a ring of NBUF chunk buffers, runs the
-//               in-chunk gate sweep ahead, checks V
-// One workgroup barrier per chunk.
+//               columns, from H_in and R the chain waves leave in LDS and P (and Q, when
+//               it fits in the ring) from the chunk buffer; otherwise it loads Q itself
+//   wave 3      loader: copies K, Q, P, V and the gate / beta rows of chunk
+//               ci + NBUF - 1 global -> LDS directly (no register round trip) into a ring
+//               of NBUF chunk buffers, runs the in-chunk gate sweep ahead, checks V
+// One workgroup barrier per chunk.  The fused composition adds two tile waves that form T
+// and P in the workgroup (described with their code below).
 //
 // State rows are stored permuted within each 32-key block: accumulator tile t = 2 kb + h,
 // row 4 g + j holds key dim pi = 32 kb + 8 g + 4 h + j.  Two stacked accumulator tiles are
