@@ -405,9 +405,11 @@ def main():
     ap.add_argument("--config", default="hybrid")
     ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--compose", default="split", choices=["split", "fused"],
-                    help="split: prep kernel then scan (timed per kernel); fused: tile waves "
-                         "inside the scan workgroup, one kernel")
+    ap.add_argument("--compose", default="auto", choices=["auto", "split", "fused", "pipelined"],
+                    help="auto: the library's choice (gdn_plan_compose says which); split: prep "
+                         "kernel then scan (timed per kernel); fused: tile waves inside the scan "
+                         "workgroup, one kernel; pipelined: scan segments with the next segment's "
+                         "prep beside each")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="before each timed step, write this much scratch memory (larger than "
@@ -502,21 +504,27 @@ def main():
     qdt = gdn.BF16 if spec.qkv_dtype == "bf16" else gdn.F32
     odt_t = torch.bfloat16 if args.arm == "bf16" else torch.float32
     arm = gdn.ARM_MFMA_BF16 if args.arm == "bf16" else gdn.ARM_FOLD_F32
-    mk = lambda stages: gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else Tn, spec.hk,
-                                         spec.hv, spec.dk, spec.dv, gate, chunk, qdt,
-                                         gdn.BF16 if odt_t == torch.bfloat16 else gdn.F32, arm,
-                                         gdn.COMPOSE_FUSED if fused else gdn.COMPOSE_SPLIT, stages)
-    fused = args.compose == "fused"
-    p_prep, p_scan = mk(gdn.STAGE_PREP), mk(gdn.STAGE_SCAN)
-    p_all = mk(gdn.STAGE_ALL)
+    req = {"auto": gdn.COMPOSE_AUTO, "split": gdn.COMPOSE_SPLIT, "fused": gdn.COMPOSE_FUSED,
+           "pipelined": gdn.COMPOSE_PIPELINED}[args.compose]
+    mk = lambda compose, stages: gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else Tn, spec.hk,
+                                                  spec.hv, spec.dk, spec.dv, gate, chunk, qdt,
+                                                  gdn.BF16 if odt_t == torch.bfloat16 else gdn.F32, arm,
+                                                  compose, stages)
+    p_all = mk(req, gdn.STAGE_ALL)
+    composition = {gdn.COMPOSE_SPLIT: "split", gdn.COMPOSE_FUSED: "fused",
+                   gdn.COMPOSE_PIPELINED: "pipelined"}[gdn.plan_compose(p_all)]
+    fused, whole = composition == "fused", composition != "split"
+    # the split composition's two stages, called one by one: the per-kernel timing
+    p_prep, p_scan = mk(gdn.COMPOSE_SPLIT, gdn.STAGE_PREP), mk(gdn.COMPOSE_SPLIT, gdn.STAGE_SCAN)
     o = torch.empty((B, Tn, spec.hv, spec.dv), dtype=odt_t, device=dev)
     hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(1, gdn.workspace_bytes(p_all if fused else p_prep)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, gdn.workspace_bytes(p_all), gdn.workspace_bytes(p_prep)), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if fused:  # one kernel (plus the chunk table of a packed batch): no stage split
+    def step(ev=None, per_kernel=False):
+        if whole and not per_kernel:  # one call (fused: one kernel; pipelined: its segments)
             if ev is not None:
                 ev[0].record(stream)
                 ev[1].record(stream)
@@ -561,6 +569,18 @@ def main():
     scan_v = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ms_step = float(np.median(step_ms))
     prep_ms, scan_ms = float(np.median(prep_v)), float(np.median(scan_v))
+    if composition == "pipelined":
+        # per-kernel times (the roofline's dominant kernel): the split composition's two
+        # stages, timed the same way in a second pass of as many cache-cold steps
+        step(per_kernel=True)  # untimed: first use of the split kernels' launch attributes
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(i & 0xFF)
+            step(kev[i], per_kernel=True)
+        torch.cuda.synchronize()
+        prep_ms = float(np.median([e[0].elapsed_time(e[1]) for e in kev]))
+        scan_ms = float(np.median([e[1].elapsed_time(e[2]) for e in kev]))
     # warm-cache median for context (same work, no eviction in between)
     wev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, args.steps // 2))]
     for e in wev:
@@ -569,8 +589,9 @@ def main():
     warm_ms = float(np.median([e[0].elapsed_time(e[2]) for e in wev]))
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
-    log("ms/step %.4f median cold (min %.4f; prep %.4f, scan %.4f), warm %.4f, wall %.3f s for %d steps"
-        % (ms_step, step_ms.min(), prep_ms, scan_ms, warm_ms, wall, args.steps))
+    log("%s: ms/step %.4f median cold (min %.4f; %sprep %.4f, scan %.4f), warm %.4f, wall %.3f s for %d steps"
+        % (composition, ms_step, step_ms.min(), "split kernels: " if composition == "pipelined" else "",
+           prep_ms, scan_ms, warm_ms, wall, args.steps))
 
     alg = algorithmic(spec, chunk)
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if args.arm == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -602,10 +623,11 @@ def main():
                                % (spec.name, spec.n_seq, spec.tokens // spec.n_seq, spec.hk, spec.hv,
                                   spec.dk, "per-head" if gate == gdn.GATE_HEAD else "per-key-channel",
                                   chunk, ", h0" if spec.h0 else ""),
-                   "tokens": spec.tokens, "arm": args.arm, "composition": args.compose},
+                   "tokens": spec.tokens, "arm": args.arm, "composition": composition},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel_ms": dom_ms, "algorithmic_bytes": dom_bytes},
+                     "traffic": traffic, "kernel_ms": dom_ms, "algorithmic_bytes": dom_bytes,
+                     "composition": "fused" if fused else "split"},
         "mfma": {"definition": "algorithmic flops / kernel time / dense peak",
                  "peak_tflops": peak_mfma,
                  "prep_frac": (alg["prep_flops"] / (prep_ms * 1e-3) / (peak_mfma * 1e12)) if not fused else None,
@@ -613,7 +635,8 @@ def main():
                  / (peak_mfma * 1e12),
                  "layer_frac": (alg["prep_flops"] + alg["scan_flops"]) / (ms_step * 1e-3)
                  / (peak_mfma * 1e12)},
-        "kernels_ms": {"prep": prep_ms, "scan": scan_ms} if not fused else {"scan_fused": scan_ms},
+        "kernels_ms": ({"prep": prep_ms, "scan": scan_ms} if not fused else {"scan_fused": scan_ms}),
+        "kernels_composition": "fused" if fused else "split",
         "timing": {"headline": "median cold-cache step (%d MiB scratch written before each step)"
                                % args.flush_mib if args.flush_mib else "median warm step",
                    "min_ms": float(step_ms.min()), "warm_median_ms": warm_ms},

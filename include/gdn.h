@@ -66,11 +66,16 @@ enum { GDN_ARM_MFMA_BF16 = 0, GDN_ARM_FOLD_F32 = 1 };
 /* Kernel composition: split (a sequence-parallel prep kernel writes every chunk's T and
  * P to the workspace, then the scan reads them) or fused (two extra waves of each scan
  * workgroup form T and P a chunk ahead and hand them over in LDS; no tile round trip
- * through HBM, but the tiles are formed once per 32-column slice of the state).  The
- * two give bit-identical results.  FUSED is built for the per-head gate with bf16
- * q/k/v on the bf16 arm (GDN_E_UNSUPPORTED otherwise) and has no separate stages.  AUTO
- * picks the measured default: split. */
-enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2 };
+ * through HBM, but the tiles are formed once per 32-column slice of the state), or
+ * pipelined (split, with the scan cut into chunk-aligned segments that carry the state
+ * through the workspace; the launch that scans segment s also runs the prep of segment
+ * s + 1 in workgroups after the scan's own, on the compute units the scan leaves idle,
+ * so only the first segment's prep is exposed).  All three give bit-identical results.
+ * FUSED is built for the per-head gate with bf16 q/k/v on the bf16 arm; PIPELINED for
+ * the per-head gate on fixed-length batches (GDN_E_UNSUPPORTED otherwise); neither has
+ * separate stages.  AUTO picks the measured default: pipelined where it applies and the
+ * scan grid leaves at least a quarter of its own size idle, else split. */
+enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2, GDN_COMPOSE_PIPELINED = 3 };
 /* Stages of the split composition a call runs.  0 (or PREP|SCAN) runs both.  A
  * SCAN-only call consumes the chunk tiles a previous PREP call (same problem, same
  * inputs, same workspace) left in the workspace; the caller orders the two calls,
@@ -103,6 +108,12 @@ gdn_status gdn_validate(const gdn_problem* p);
 /* Bytes of device workspace gdn_chunk_fwd needs for *p (written to *bytes).
  * Same return codes as gdn_validate. */
 gdn_status gdn_workspace_bytes(const gdn_problem* p, size_t* bytes);
+
+/* The composition gdn_chunk_fwd runs for *p on the current device (written to *compose:
+ * GDN_COMPOSE_SPLIT, _FUSED or _PIPELINED): the requested one, or for GDN_COMPOSE_AUTO the
+ * library's choice, which depends on the device's compute-unit count.  Host-only (a
+ * device attribute query, no device work); same return codes as gdn_validate. */
+gdn_status gdn_plan_compose(const gdn_problem* p, int32_t* compose);
 
 /*
  * gdn_chunk_fwd -- chunkwise gated delta-rule prefill.

@@ -27,7 +27,7 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   if (p->o_dtype != GDN_BF16 && p->o_dtype != GDN_F32) return GDN_E_UNSUPPORTED;
   if (p->arm != GDN_ARM_MFMA_BF16 && p->arm != GDN_ARM_FOLD_F32) return GDN_E_UNSUPPORTED;
   if (p->compose != GDN_COMPOSE_AUTO && p->compose != GDN_COMPOSE_SPLIT &&
-      p->compose != GDN_COMPOSE_FUSED)
+      p->compose != GDN_COMPOSE_FUSED && p->compose != GDN_COMPOSE_PIPELINED)
     return GDN_E_UNSUPPORTED;
   if (p->stages < 0 || p->stages > (GDN_STAGE_PREP | GDN_STAGE_SCAN)) return GDN_E_UNSUPPORTED;
   // the fused composition (tile waves inside the scan workgroup) is built for the
@@ -37,6 +37,11 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
        !(p->stages == GDN_STAGE_ALL || p->stages == (GDN_STAGE_PREP | GDN_STAGE_SCAN))))
     return GDN_E_UNSUPPORTED;
 
+  // the pipelined composition (scan segments carrying the state, the next segment's
+  // prep beside each) is built for the per-head gate on fixed-length batches, all stages
+  const bool pipe_ok = p->gate == GDN_GATE_HEAD && p->seq_len > 0 &&
+                       (p->stages == GDN_STAGE_ALL || p->stages == (GDN_STAGE_PREP | GDN_STAGE_SCAN));
+  if (p->compose == GDN_COMPOSE_PIPELINED && !pipe_ok) return GDN_E_UNSUPPORTED;
   Plan pl;
   memset(&pl, 0, sizeof(pl));
   pl.n_seq = p->n_seq;
@@ -52,6 +57,8 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   pl.qkv_f32 = p->qkv_dtype == GDN_F32;
   pl.o_f32 = p->o_dtype == GDN_F32;
   pl.fused = p->compose == GDN_COMPOSE_FUSED;
+  pl.pipe_ok = pipe_ok && (p->compose == GDN_COMPOSE_AUTO || p->compose == GDN_COMPOSE_PIPELINED);
+  pl.pipe_req = p->compose == GDN_COMPOSE_PIPELINED ? 1 : (p->compose == GDN_COMPOSE_AUTO ? -1 : 0);
   pl.run_prep = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_PREP);
   pl.run_scan = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_SCAN);
   // The fixed-length form is chosen when seq_len > 0 or when there are no tokens at all;
@@ -96,6 +103,10 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   off = round_up(off + kq, 256);
   pl.off_Q = off;
   off = round_up(off + kq, 256);
+  // pipelined composition: the state carried from one scan segment to the next
+  const size_t carry = pl.pipe_ok ? (size_t)pl.n_seq * pl.hv * pl.dk * pl.dv * 4 : 0;
+  pl.off_carry = off;
+  off = round_up(off + carry, 256);
   pl.bytes = off;
   *out = pl;
   return GDN_OK;
@@ -118,6 +129,14 @@ gdn_status gdn_validate(const gdn_problem* p) {
   return gdn::make_plan(p, &pl);
 }
 
+gdn_status gdn_plan_compose(const gdn_problem* p, int32_t* compose) {
+  if (!compose) return GDN_E_NULL;
+  gdn::Plan pl;
+  gdn_status s = gdn::make_plan(p, &pl);
+  if (s != GDN_OK) return s;
+  *compose = gdn::plan_compose(pl);
+  return GDN_OK;
+}
 gdn_status gdn_workspace_bytes(const gdn_problem* p, size_t* bytes) {
   if (!bytes) return GDN_E_NULL;
   gdn::Plan pl;
@@ -199,7 +218,13 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   prm.varlen = pl.varlen;
   prm.chunks_per_seq = pl.chunks_per_seq;
   prm.max_slots = pl.max_slots;
-  return gdn::launch(pl, prm, stream);
+  prm.seg_cb = 0;
+  prm.seg_ce = pl.varlen ? INT32_MAX : pl.chunks_per_seq;
+  prm.prep_cb = 0;
+  prm.prep_ce = prm.seg_ce;
+  prm.nscan = (int32_t)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
+  prm.h0_input = 1;
+  return gdn::launch(pl, prm, ws ? ws + pl.off_carry : nullptr, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,

@@ -28,13 +28,16 @@ struct Plan {
   int32_t arm_f32;       // 1: fp32-fold arm
   int32_t qkv_f32, o_f32;
   int32_t fused;         // 1: fused composition
+  int32_t pipe_ok;       // pipelined composition possible and not excluded by the request
+                         // (per-head gate, fixed length, all stages, AUTO or PIPELINED)
+  int32_t pipe_req;      // 1: pipelined requested, 0: split requested, -1: library choice
   int32_t run_prep, run_scan;  // stages to launch
   int32_t varlen;        // 1: cu_seqlens given
   int32_t chunks_per_seq;  // fixed-length batches
   int64_t max_slots;     // chunk slots the prep grid covers
   // workspace carve-up (byte offsets)
   int32_t kq_ws;         // 1: K and Q copied to the workspace in the arm's type
-  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, bytes;
+  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, off_carry, bytes;
 };
 
 // Kernel arguments (by value).
@@ -60,6 +63,12 @@ struct Params {
   int32_t n_seq, seq_len, hk, hv, dv;
   int32_t qkv_f32, o_f32, varlen, chunks_per_seq, kq_ws;
   int64_t max_slots;
+  // Chunk ranges of one launch (fixed-length batches; the whole sequence otherwise):
+  // the scan walks chunks [seg_cb, seg_ce) of every sequence starting from h0 (checked
+  // for Inf/NaN only when h0_input) and ends with hT; the prep covers chunks
+  // [prep_cb, prep_ce).  Scan workgroups are blockIdx < nscan; in the pipelined
+  // composition the workgroups after them run the prep of the next segment.
+  int32_t seg_cb, seg_ce, prep_cb, prep_ce, nscan, h0_input;
 };
 
 // Arguments of the one-token recurrent step (by value).
@@ -79,6 +88,8 @@ struct DecodeParams {
 
 gdn_status make_plan(const gdn_problem* p, Plan* plan);
 gdn_status launch_decode(const DecodeParams& prm, int dk, bool per_channel_gate, void* stream);
-gdn_status launch(const Plan& plan, const Params& prm, void* stream);
+gdn_status launch(const Plan& plan, const Params& prm, void* carry, void* stream);
+// the composition launch() runs for this plan on the current device (GDN_COMPOSE_*)
+int32_t plan_compose(const Plan& plan);
 
 }  // namespace gdn

@@ -288,6 +288,21 @@ __device__ __forceinline__ bool locate_chunk(const Params& p, int C, int64_t slo
   return L > 0;
 }
 
+// The m-th chunk slot of a launch's prep range: every slot, or for a fixed-length batch
+// chunks [prep_cb, prep_ce) of each sequence in turn.  False past the range.
+__device__ __forceinline__ bool prep_slot(const Params& p, int64_t m, int64_t& slot) {
+  if (p.varlen) {
+    slot = m;
+    return m < p.max_slots;
+  }
+  const int pw = p.prep_ce - p.prep_cb;
+  if (pw <= 0) return false;
+  const int64_t n = m / pw;
+  if (n >= p.n_seq) return false;
+  slot = n * p.chunks_per_seq + p.prep_cb + (m - n * pw);
+  return true;
+}
+
 // ---------------------------------------------------- chunk table --------
 // Sanitised bounds b_0 = 0, b_i = min(total, max(0, max_{1<=j<=i} cu_j)), b_n = total,
 // so every index stays inside [0, total] whatever cu_seqlens holds; any difference
@@ -715,41 +730,42 @@ __device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int la
   return bad;
 }
 
-// Per-head gate: one wave per (chunk slot, value head), no barrier.  A workgroup holds up
-// to 4 value heads of one key head (blockDim = 64 * min(group, 4)), so the waves that read
-// the same K and Q rows run side by side on one CU and fetch them from HBM once.  Every
-// global load is issued first, then the math.
+// One (chunk slot, value head) unit of the per-head-gate prep on one wave, in two
+// halves: prep_fetch issues its global loads (false for a slot past the last chunk),
+// prep_finish does the rest with the wave's solve scratch S -- the gate sweep, K K^T and
+// Q K^T, A and P, the solve, and T and P stored as scan fragments.  Only the first value
+// head of a key head's group checks K and Q and (kq_ws) writes them in the arm's type.
+template <int DK, int C, bool QF32>
+struct PrepUnit {
+  TileRegs<DK, C, QF32> R;
+  int64_t slot, t0;
+  int kh, j, L;
+};
+
+template <int DK, int C, bool QF32>
+__device__ __forceinline__ bool prep_fetch(const Params& p, int64_t slot, int kh, int j, int lane,
+                                           PrepUnit<DK, C, QF32>& U) {
+  int n;
+  if (!locate_chunk(p, C, slot, n, U.t0, U.L)) return false;
+  U.slot = slot;
+  U.kh = kh;
+  U.j = j;
+  tile_loads<DK, C, QF32>(p, U.t0, U.L, kh, kh * (p.hv / p.hk) + j, lane, U.R);
+  return true;
+}
+
 template <class Arm, int DK, int C, bool QF32>
-__global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
+__device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, C, QF32>& U, int lane, float* S) {
   using SL = SolveLds<C>;
   constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32;
-  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
-  const int group = p.hv / p.hk, wpb = blockDim.x >> 6, nblk = (group + wpb - 1) / wpb;
-  // Workgroups go to the 8 XCDs round-robin: XCD x = blockIdx % 8 takes the chunk slots
-  // x, x + 8, ..., all key heads of a slot together, so the gate and beta rows of a chunk
-  // (every head's values of a token share a cache line) are fetched into one L2 only.
-  // The grid is padded to whole groups of 8 slots; workgroups past the last slot exit.
-  const int ipp = p.hk * nblk;  // workgroups per slot
-  const int64_t pos = blockIdx.x / 8;
-  const int r = (int)(pos % ipp);
-  const int jb = r % nblk;
-  const int kh = r / nblk;
-  const int64_t slot = (pos / ipp) * 8 + blockIdx.x % 8;
-  const int j = jb * wpb + w;  // value head inside the key head's group
-  int n, L;
-  int64_t t0;
-  if (j >= group || slot >= p.max_slots || !locate_chunk(p, C, slot, n, t0, L)) return;
-  const int h = kh * group + j;
-  float* S = (float*)gdn_smem + w * SL::FLOATS;
+  const int i = lane & 15, g = lane >> 4;
+  const int kh = U.kh, j = U.j, L = U.L, h = kh * (p.hv / p.hk) + j;
+  const int64_t slot = U.slot;
   float* Gs = S + NTRI * kTile;
   float* Bs = Gs + C;
-
-  TileRegs<DK, C, QF32> R;
-  tile_loads<DK, C, QF32>(p, t0, L, kh, h, lane, R);
-  uint32_t bad = tile_sweep<C>(R.xl, R.bl, L, lane, Gs, Bs);
+  uint32_t bad = tile_sweep<C>(U.R.xl, U.R.bl, L, lane, Gs, Bs);
   if (j == 0) {  // once per key head (wave-uniform)
-    bad |= tile_kq_nonfinite<DK, C, QF32>(R);
+    bad |= tile_kq_nonfinite<DK, C, QF32>(U.R);
     if (p.kq_ws) {
       // K and Q in the arm's element type, [slot][key head][C][DK], for the scan (inputs
       // in fp32, or the fp32 arm); rows past the chunk end repeat its last row
@@ -761,17 +777,146 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
           const int o = (16 * rt + i) * DK + 32 * kb + 8 * g;
-          Arm::stf(kc + o, frag_of<Arm, QF32>(R.rk[kb][rt]));
-          Arm::stf(qc + o, frag_of<Arm, QF32>(R.rq[kb][rt]));
+          Arm::stf(kc + o, frag_of<Arm, QF32>(U.R.rk[kb][rt]));
+          Arm::stf(qc + o, frag_of<Arm, QF32>(U.R.rq[kb][rt]));
         }
     }
   }
   f32x4 accA[NTRI], accP[NTRI];
-  tile_products<Arm, DK, C, QF32>(R, accA, accP);
+  tile_products<Arm, DK, C, QF32>(U.R, accA, accP);
   typedef typename Arm::T T;
   const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
   wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
   if (bad) atomicOr(p.status, bad);
+}
+
+// Per-head gate: one wave per (chunk slot, value head), no barrier.  A workgroup holds up
+// to 4 value heads of one key head (blockDim = 64 * min(group, 4)), so the waves that read
+// the same K and Q rows run side by side on one CU and fetch them from HBM once.  Every
+// global load is issued first, then the math.
+template <class Arm, int DK, int C, bool QF32>
+__global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
+  using SL = SolveLds<C>;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
+  const int group = p.hv / p.hk, wpb = blockDim.x >> 6, nblk = (group + wpb - 1) / wpb;
+  // Workgroups go to the 8 XCDs round-robin: XCD x = blockIdx % 8 takes the chunk slots
+  // x, x + 8, ... of the launch's range, all key heads of a slot together, so the gate
+  // and beta rows of a chunk (every head's values of a token share a cache line) are
+  // fetched into one L2 only.  The grid is padded to whole groups of 8 slots; workgroups
+  // past the last slot exit.
+  const int ipp = p.hk * nblk;  // workgroups per slot
+  const int64_t pos = blockIdx.x / 8;
+  const int r = (int)(pos % ipp);
+  const int jb = r % nblk;
+  const int kh = r / nblk;
+  const int64_t m = (pos / ipp) * 8 + blockIdx.x % 8;
+  const int j = jb * wpb + w;  // value head inside the key head's group
+  int64_t slot;
+  if (j >= group || !prep_slot(p, m, slot)) return;
+  PrepUnit<DK, C, QF32> U;
+  if (prep_fetch<DK, C, QF32>(p, slot, kh, j, lane, U))
+    prep_finish<Arm, DK, C, QF32>(p, U, lane, (float*)gdn_smem + w * SL::FLOATS);
+}
+
+// The prep of the next scan segment, run by the workgroups of a pipelined scan launch
+// after the scan's own (blockIdx >= nscan, a multiple of 8, so these workgroups too sit
+// on XCD blockIdx % 8).  They stay resident and loop: wave w of prep workgroup b takes
+// units (slot of the range, key head), key head fastest, among the slots m = x, x + 8,
+// ... that belong to its XCD x, with a stride of all the XCD's prep waves.  A unit loads
+// K and Q and forms K K^T and Q K^T once, then gates, solves and stores the tiles of each
+// value head of the key head's group from a copy of the two products: the same
+// instructions on the same values as the prep kernel, so the same bits.  (fp32 inputs or
+// operands: units of one value head, like the prep kernel's waves.)
+template <class Arm, int DK, int C, bool QF32>
+__device__ __forceinline__ void prep_role(const Params& p) {
+  using SL = SolveLds<C>;
+  constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32, GPRE = 4;
+  typedef typename Arm::T T;
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
+  const int pb = (int)blockIdx.x - p.nscan, npb = (int)gridDim.x - p.nscan;
+  const int x = pb % 8, group = p.hv / p.hk;
+  const int64_t M = (int64_t)p.n_seq * (p.prep_ce - p.prep_cb);
+  const int64_t stride = (int64_t)((npb - x + 7) / 8) * nw;
+  float* S = (float*)gdn_smem + w * SL::FLOATS;
+  if constexpr (QF32 || sizeof(T) == 4) {
+    // fp32 inputs or operands: the load registers alone fill half the register file, so
+    // one (slot, value head) unit at a time, as in the prep kernel
+    const int64_t units = (M - x + 7) / 8 * p.hv;
+    for (int64_t z = (int64_t)(pb / 8) * nw + w; z < units; z += stride) {
+      const int64_t k = z / p.hv;
+      const int h = (int)(z - k * p.hv);
+      int64_t slot;
+      PrepUnit<DK, C, QF32> U;
+      if (prep_slot(p, 8 * k + x, slot) && prep_fetch<DK, C, QF32>(p, slot, h / group, h % group, lane, U))
+        prep_finish<Arm, DK, C, QF32>(p, U, lane, S);
+    }
+    return;
+  }
+  const int64_t units = (M - x + 7) / 8 * p.hk;
+  float* Gs = S + NTRI * kTile;
+  float* Bs = Gs + C;
+  for (int64_t z = (int64_t)(pb / 8) * nw + w; z < units; z += stride) {
+    const int64_t k = z / p.hk;
+    const int kh = (int)(z - k * p.hk);
+    int64_t slot, t0;
+    int n, L;
+    if (!prep_slot(p, 8 * k + x, slot) || !locate_chunk(p, C, slot, n, t0, L)) continue;
+    const int h0 = kh * group, rg = lane < L ? lane : L - 1;
+    TileRegs<DK, C, QF32> R;
+    tile_loads<DK, C, QF32>(p, t0, L, kh, h0, lane, R);
+    float xs[GPRE], bs[GPRE];  // gate and beta rows of the group's first value heads
+    xs[0] = R.xl;
+    bs[0] = R.bl;
+#pragma unroll
+    for (int j = 1; j < GPRE; ++j)
+      if (j < group) {
+        xs[j] = p.g[(t0 + rg) * p.hv + h0 + j];
+        bs[j] = p.beta[(t0 + rg) * p.hv + h0 + j];
+      }
+    uint32_t bad = tile_kq_nonfinite<DK, C, QF32>(R);
+    if (p.kq_ws) {  // K and Q in the arm's element type (as in prep_finish)
+      T* kc = (T*)p.Kws + (slot * p.hk + kh) * (int64_t)(C * DK);
+      T* qc = (T*)p.Qws + (slot * p.hk + kh) * (int64_t)(C * DK);
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int o = (16 * rt + i) * DK + 32 * kb + 8 * g;
+          Arm::stf(kc + o, frag_of<Arm, QF32>(R.rk[kb][rt]));
+          Arm::stf(qc + o, frag_of<Arm, QF32>(R.rq[kb][rt]));
+        }
+    }
+    f32x4 A0[NTRI], P0[NTRI];
+    tile_products<Arm, DK, C, QF32>(R, A0, P0);
+    for (int j = 0; j < group; ++j) {
+      float xl, bl;
+      if (j < GPRE) {
+        xl = xs[0];
+        bl = bs[0];
+#pragma unroll
+        for (int jj = 1; jj < GPRE; ++jj)
+          if (j == jj) {
+            xl = xs[jj];
+            bl = bs[jj];
+          }
+      } else {
+        xl = p.g[(t0 + rg) * p.hv + h0 + j];
+        bl = p.beta[(t0 + rg) * p.hv + h0 + j];
+      }
+      bad |= tile_sweep<C>(xl, bl, L, lane, Gs, Bs);
+      f32x4 accA[NTRI], accP[NTRI];
+#pragma unroll
+      for (int t = 0; t < NTRI; ++t) {
+        accA[t] = A0[t];
+        accP[t] = P0[t];
+      }
+      const int64_t tofs = (slot * p.hv + h0 + j) * (int64_t)tile_elems(C);
+      wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
+    }
+    if (bad) atomicOr(p.status, bad);
+  }
 }
 
 // Per-channel gate (C = 32): one workgroup per (chunk slot, value head).  The gate sweep
@@ -1122,6 +1267,12 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   using Lay = OpLayout<Arm, DK>;
   using SL = ScanLds<Arm, DK, C, KDA, QF32, FUSED>;
   static_assert(!FUSED || (!KDA && !QF32), "fused composition: per-head gate, bf16 inputs");
+  if constexpr (!KDA && !FUSED) {
+    if ((int)blockIdx.x >= p.nscan) {  // pipelined composition: the next segment's prep
+      prep_role<Arm, DK, C, QF32>(p);
+      return;
+    }
+  }
   constexpr int NT = C / 16, NBC = C / 32, NTK = DK / 16, NBK = DK / 32;
   constexpr int NBUF = SL::NBUF, LA = NBUF - 1;  // loader copies LA chunks ahead
   constexpr int CL = SL::CL;                      // ... and keeps CL chunks complete ahead
@@ -1149,7 +1300,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     h = ((r / gs) * 8 + x) * group + r2 / nslice;
     slice = r2 % nslice;
   } else {
-    const int nb = (int)gridDim.x, per = nb / 8, rem = nb % 8;
+    const int nb = p.nscan, per = nb / 8, rem = nb % 8;
     const int x = (int)blockIdx.x % 8, pos = (int)blockIdx.x / 8;
     int bid = x * per + (x < rem ? x : rem) + pos;
     slice = bid % nslice;
@@ -1164,10 +1315,11 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     s0 = p.table[n];
     s1 = p.table[n + 1];
     slot0 = p.table[p.n_seq + 1 + n];
-  } else {
-    s0 = (int64_t)n * p.seq_len;
-    s1 = s0 + p.seq_len;
-    slot0 = (int64_t)n * p.chunks_per_seq;
+  } else {  // this launch's chunks [seg_cb, seg_ce) of the sequence
+    const int64_t b = (int64_t)n * p.seq_len;
+    s0 = b + min64(p.seq_len, (int64_t)p.seg_cb * C);
+    s1 = b + min64(p.seq_len, (int64_t)p.seg_ce * C);
+    slot0 = (int64_t)n * p.chunks_per_seq + p.seg_cb;
   }
   const int nch = (int)((s1 - s0 + C - 1) / C);
   uint32_t bad = 0;
@@ -1498,7 +1650,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           H[t][j] = p.h0[hbase + (int64_t)state_dim(t, g, j) * DV + col0];
-          bad |= flag_if(f_nonfinite(H[t][j]), GDN_ST_NONFINITE_INPUT);
+          bad |= flag_if(p.h0_input && f_nonfinite(H[t][j]), GDN_ST_NONFINITE_INPUT);
         }
     } else {
 #pragma unroll
@@ -1768,8 +1920,73 @@ bool set_lds_once(Fn fn, size_t lds) {
   return true;
 }
 
+// Pipelined composition: the scan in chunk-aligned segments (the state carried in
+// `carry`), each launch also running the next segment's prep in workgroups after the
+// scan's own.  Segments are kSegChunks chunks long (the last one may be shorter): on the
+// hybrid layer (512 chunks) 16 segments of 32 measured 0.748 ms, against 0.844 with 8,
+// 0.790 with 12, 0.826 with 32 and 0.922 for the split composition.
+constexpr int kSegChunks = 32;
+
+template <class Arm, int DK, int C, bool QF32>
+gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int nprep, hipStream_t st) {
+  const int cps = pl.chunks_per_seq;
+  const int S = (cps + kSegChunks - 1) / kSegChunks;
+  auto cut = [&](int s) { return s < S ? s * kSegChunks : cps; };
+  const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
+  if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
+  using SL = ScanLds<Arm, DK, C, false, QF32, false>;
+  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false>, SL::BYTES)) return GDN_E_LAUNCH;
+  Params q = prm;
+  q.prep_cb = 0;
+  q.prep_ce = cut(1);
+  const int64_t m0 = (int64_t)pl.n_seq * q.prep_ce;  // 0 when the first segment is empty
+  if (m0 > 0) {
+    hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)((m0 + 7) / 8 * 8 * pl.hk * nblk)),
+                       dim3(64 * wpb), wpb * SolveLds<C>::FLOATS * sizeof(float), st, q);
+    if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
+  }
+  for (int s = 0; s < S; ++s) {
+    const bool last = s == S - 1;
+    q.seg_cb = cut(s);
+    q.seg_ce = cut(s + 1);
+    q.prep_cb = last ? 0 : cut(s + 1);
+    q.prep_ce = last ? 0 : cut(s + 2);
+    q.h0 = s == 0 ? prm.h0 : carry;
+    q.h0_input = s == 0;
+    q.hT = last ? prm.hT : carry;
+    const int grid = q.nscan + (last ? 0 : nprep);
+    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false>), dim3((unsigned)grid), dim3(256), SL::BYTES, st, q);
+    if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
+  }
+  return GDN_OK;
+}
+
+// Workgroups a pipelined launch gives the next segment's prep: the compute units the
+// scan leaves idle (one scan workgroup fills a unit's LDS), in whole groups of 8 (one per
+// XCD); 0 when the pipelined composition does not apply or would not pay.
+int pipelined_prep_wgs(const Plan& pl, int nscan) {
+  if (!pl.pipe_ok || pl.pipe_req == 0) return 0;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 0;
+  int nprep = (ncu - nscan) / 8 * 8;
+  if (pl.pipe_req == 1) return nprep >= 8 ? nprep : 8;  // requested: runs (correctly) even on a full device
+  // library choice: at least four segments (with fewer, the first segment's prep, which
+  // nothing hides, is too large a share: the single 4,096-token layer, 64 chunks, measured
+  // 7 % slower pipelined), an XCD-aligned scan grid, and a prep share of at least a
+  // quarter of the scan's
+  if (pl.chunks_per_seq < 4 * kSegChunks || nscan % 8 != 0 || pl.hk % 8 != 0 || nprep < 8 || 4 * nprep < nscan)
+    return 0;
+  return nprep;
+}
+
 template <class Arm, int DK, int C, bool KDA, bool QF32>
-gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
+gdn_status run(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
+  if constexpr (!KDA) {  // the same decision as plan_compose()
+    const int nprep = pipelined_prep_wgs(pl, prm.nscan);
+    if (nprep > 0 && pl.run_prep && pl.run_scan && pl.max_slots > 0)
+      return run_pipelined<Arm, DK, C, QF32>(pl, prm, (float*)carry, nprep, st);
+  }
   if (pl.run_prep && !pl.fused && pl.max_slots > 0) {
     if constexpr (KDA) {
       const size_t lds = prep_chan_lds_bytes<Arm, DK>();
@@ -1805,39 +2022,47 @@ gdn_status run(const Plan& pl, const Params& prm, hipStream_t st) {
 }
 
 template <class Arm, int DK, bool QF32>
-gdn_status run_dk(const Plan& pl, const Params& prm, hipStream_t st) {
-  if (pl.gate_channel) return run<Arm, DK, 32, true, QF32>(pl, prm, st);
-  if (pl.chunk == 32) return run<Arm, DK, 32, false, QF32>(pl, prm, st);
-  return run<Arm, DK, 64, false, QF32>(pl, prm, st);
+gdn_status run_dk(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
+  if (pl.gate_channel) return run<Arm, DK, 32, true, QF32>(pl, prm, carry, st);
+  if (pl.chunk == 32) return run<Arm, DK, 32, false, QF32>(pl, prm, carry, st);
+  return run<Arm, DK, 64, false, QF32>(pl, prm, carry, st);
 }
 
 template <class Arm>
-gdn_status run_arm(const Plan& pl, const Params& prm, hipStream_t st) {
+gdn_status run_arm(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
   if (pl.qkv_f32) {
     switch (pl.dk) {
-      case 32: return run_dk<Arm, 32, true>(pl, prm, st);
-      case 64: return run_dk<Arm, 64, true>(pl, prm, st);
-      case 128: return run_dk<Arm, 128, true>(pl, prm, st);
+      case 32: return run_dk<Arm, 32, true>(pl, prm, carry, st);
+      case 64: return run_dk<Arm, 64, true>(pl, prm, carry, st);
+      case 128: return run_dk<Arm, 128, true>(pl, prm, carry, st);
       default: return GDN_E_UNSUPPORTED;
     }
   }
   switch (pl.dk) {
-    case 32: return run_dk<Arm, 32, false>(pl, prm, st);
-    case 64: return run_dk<Arm, 64, false>(pl, prm, st);
-    case 128: return run_dk<Arm, 128, false>(pl, prm, st);
+    case 32: return run_dk<Arm, 32, false>(pl, prm, carry, st);
+    case 64: return run_dk<Arm, 64, false>(pl, prm, carry, st);
+    case 128: return run_dk<Arm, 128, false>(pl, prm, carry, st);
     default: return GDN_E_UNSUPPORTED;
   }
 }
 
 }  // namespace
 
-gdn_status launch(const Plan& pl, const Params& prm, void* stream) {
+int32_t plan_compose(const Plan& pl) {
+  if (pl.fused) return GDN_COMPOSE_FUSED;
+  const int nscan = (int)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
+  if (!pl.gate_channel && pl.run_prep && pl.run_scan && pl.max_slots > 0 && pipelined_prep_wgs(pl, nscan) > 0)
+    return GDN_COMPOSE_PIPELINED;
+  return GDN_COMPOSE_SPLIT;
+}
+
+gdn_status launch(const Plan& pl, const Params& prm, void* carry, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (pl.varlen && (pl.run_prep || pl.fused)) {
     hipLaunchKernelGGL(gdn_chunk_table, dim3(1), dim3(256), 0, st, prm, (int)pl.chunk);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
-  return pl.arm_f32 ? run_arm<ArmF32>(pl, prm, st) : run_arm<ArmBF16>(pl, prm, st);
+  return pl.arm_f32 ? run_arm<ArmF32>(pl, prm, carry, st) : run_arm<ArmBF16>(pl, prm, carry, st);
 }
 
 }  // namespace gdn

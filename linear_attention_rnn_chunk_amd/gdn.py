@@ -25,11 +25,11 @@ ST_NONFINITE_OUTPUT = 0x8
 GATE_HEAD, GATE_KEY_CHANNEL = 0, 1
 BF16, F32 = 0, 1
 ARM_MFMA_BF16, ARM_FOLD_F32 = 0, 1
-COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED = 0, 1, 2
+COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED, COMPOSE_PIPELINED = 0, 1, 2, 3
 STAGE_ALL, STAGE_PREP, STAGE_SCAN = 0, 1, 2
 
 # every symbol include/gdn.h declares
-EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
+EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_plan_compose", "gdn_chunk_fwd", "gdn_decode_step",
            "gdn_error_string", "gdn_status_string", "gdn_abi_version")
 
 
@@ -76,6 +76,8 @@ def load():
             lib.gdn_validate.restype = ctypes.c_int
             lib.gdn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
             lib.gdn_workspace_bytes.restype = ctypes.c_int
+            lib.gdn_plan_compose.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+            lib.gdn_plan_compose.restype = ctypes.c_int
             lib.gdn_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.c_size_t, vp]
             lib.gdn_chunk_fwd.restype = ctypes.c_int
@@ -122,13 +124,23 @@ def workspace_bytes(prob: Problem) -> int:
     return int(n.value)
 
 
+def plan_compose(prob: Problem) -> int:
+    """The composition gdn_chunk_fwd runs for `prob` on the current device (COMPOSE_*)."""
+    c = ctypes.c_int32(-1)
+    rc = load().gdn_plan_compose(ctypes.byref(prob), ctypes.byref(c))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_plan_compose")
+    return int(c.value)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
 _DT = {torch.bfloat16: BF16, torch.float32: F32}
 _ARM = {"bf16": ARM_MFMA_BF16, "f32": ARM_FOLD_F32}
-_COMPOSE = {"auto": COMPOSE_AUTO, "split": COMPOSE_SPLIT, "fused": COMPOSE_FUSED}
+_COMPOSE = {"auto": COMPOSE_AUTO, "split": COMPOSE_SPLIT, "fused": COMPOSE_FUSED,
+            "pipelined": COMPOSE_PIPELINED}
 
 
 def chunk_fwd_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT, status, workspace,

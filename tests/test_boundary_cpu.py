@@ -73,9 +73,30 @@ def P(**kw):
     (dict(compose=gdn.COMPOSE_FUSED, arm=gdn.ARM_FOLD_F32), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=gdn.COMPOSE_FUSED, stages=gdn.STAGE_PREP), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=gdn.COMPOSE_FUSED, stages=gdn.STAGE_PREP | gdn.STAGE_SCAN), gdn.GDN_OK),
+    # the pipelined composition: per-head gate, fixed-length batches, all stages, any arm
+    (dict(compose=gdn.COMPOSE_PIPELINED), gdn.GDN_OK),
+    (dict(compose=gdn.COMPOSE_PIPELINED, arm=gdn.ARM_FOLD_F32, qkv_dtype=gdn.F32), gdn.GDN_OK),
+    (dict(compose=gdn.COMPOSE_PIPELINED, stages=gdn.STAGE_PREP | gdn.STAGE_SCAN), gdn.GDN_OK),
+    (dict(compose=gdn.COMPOSE_PIPELINED, gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_PIPELINED, n_seq=3, seq_len=0), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_PIPELINED, stages=gdn.STAGE_SCAN), gdn.GDN_E_UNSUPPORTED),
 ])
 def test_validate_refusals(kw, code):
     assert gdn.validate(P(**kw)) == code
+
+
+def test_plan_compose_host_rules():
+    # explicit requests are reported as given; refused problems keep their error code;
+    # AUTO resolves to split or pipelined (the latter only where the device has idle units)
+    assert gdn.plan_compose(P(compose=gdn.COMPOSE_SPLIT)) == gdn.COMPOSE_SPLIT
+    assert gdn.plan_compose(P(compose=gdn.COMPOSE_FUSED)) == gdn.COMPOSE_FUSED
+    assert gdn.plan_compose(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32)) == gdn.COMPOSE_SPLIT
+    assert gdn.plan_compose(P(n_seq=3, seq_len=0)) == gdn.COMPOSE_SPLIT
+    assert gdn.plan_compose(P(compose=gdn.COMPOSE_AUTO)) in (gdn.COMPOSE_SPLIT, gdn.COMPOSE_PIPELINED)
+    with pytest.raises(gdn.GdnError):
+        gdn.plan_compose(P(dk=96))
+    lib = gdn.load()
+    assert lib.gdn_plan_compose(ctypes.byref(P()), None) == gdn.GDN_E_NULL
 
 
 def test_validate_null_problem():
@@ -91,13 +112,20 @@ def test_workspace_bytes_scales_with_tiles():
     # C = 32: 2 fragments, 1024), bf16 (2 B) or fp32 (4 B)
     slots, hv = 4, 6
     for C, elems in ((64, 3072), (32, 1024)):
-        b16 = gdn.workspace_bytes(P(chunk=C))
-        f32 = gdn.workspace_bytes(P(chunk=C, arm=gdn.ARM_FOLD_F32))
+        b16 = gdn.workspace_bytes(P(chunk=C, compose=gdn.COMPOSE_SPLIT))
+        f32 = gdn.workspace_bytes(P(chunk=C, arm=gdn.ARM_FOLD_F32, compose=gdn.COMPOSE_SPLIT))
         s = slots * 64 // C
         assert 2 * s * hv * elems * 2 <= b16 < 2 * s * hv * elems * 2 + 1024
         # the fp32 arm also keeps K and Q in fp32 for the scan: [slot][hk][C][dk] each
         kq = 2 * s * 2 * C * 128 * 4
         assert 2 * s * hv * elems * 4 + kq <= f32 < 2 * s * hv * elems * 4 + kq + 1024
+    # the library's choice may pipeline a fixed-length per-head-gate batch: the state
+    # carried between scan segments, [n_seq][hv][dk][dv] fp32, on top of the split tiles
+    carry = 1 * hv * 128 * 128 * 4
+    assert gdn.workspace_bytes(P()) == gdn.workspace_bytes(P(compose=gdn.COMPOSE_SPLIT)) + carry
+    assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_PIPELINED)) == gdn.workspace_bytes(P())
+    assert gdn.workspace_bytes(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32)) == \
+        gdn.workspace_bytes(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32, compose=gdn.COMPOSE_SPLIT))
     # fused composition: no tiles in the workspace (only the chunk table of a packed batch)
     assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_FUSED)) == 0
     assert 0 < gdn.workspace_bytes(P(n_seq=3, seq_len=0, compose=gdn.COMPOSE_FUSED)) <= 256
