@@ -155,6 +155,50 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds, label="hybrid",
     return trace_txt, "\n".join(lines) + "\n"
 
 
+def summarize_launches(kt_dir, cmd):
+    """The launches of one step of the default composition (the last timed step before the
+    per-kernel pass), from a per-dispatch kernel trace: each gdn kernel's duration and
+    workgroups, and the span from the first launch's start to the last one's end."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # a step is a run of gdn launches between two flushes (the scratch write before each step)
+    steps, cur = [], []
+    for r in rows:
+        if "gdn_" in r["Kernel_Name"]:
+            cur.append(r)
+        elif cur:
+            steps.append(cur)
+            cur = []
+    if cur:
+        steps.append(cur)
+    # the timed steps: the most frequent run length (warm-up and warm-cache steps run back
+    # to back and merge into longer runs; the per-kernel pass gives runs of two)
+    from collections import Counter
+    lens = Counter(len(st) for st in steps if len(st) >= 3) or Counter(len(st) for st in steps)
+    n = lens.most_common(1)[0][0] if lens else 0
+    long_steps = [st for st in steps if len(st) == n]
+    step = long_steps[len(long_steps) // 2] if long_steps else []
+    wg = lambda r: int(r.get("Grid_Size", r.get("Grid_Size_X", 0))) // max(1, int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 1))))
+    lines = ["# launches of one cache-cold step of the hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, "
+             "chunk 64) in the library's default composition",
+             "# command: " + cmd,
+             "# timed steps of %d launches in the trace: %d (the middle one shown)" % (n, len(long_steps)),
+             "kernel  workgroups  dur_us"]
+    for r in step:
+        m = re.search(r"(gdn_\w+)", r["Kernel_Name"])
+        lines.append("%s  %d  %.1f" % (m.group(1) if m else r["Kernel_Name"][:40], wg(r),
+                                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    if step:
+        span = (int(step[-1]["End_Timestamp"]) - int(step[0]["Start_Timestamp"])) / 1e3
+        busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in step) / 1e3
+        lines.append("span_us: %.1f  (sum of launch durations %.1f)" % (span, busy))
+    return "\n".join(lines) + "\n"
+
+
 PROBE_MIB = 256
 
 # one rocprofv3 --pmc pass (6 SQ counters, 1 GRBM counter: within one pass's limits)
@@ -417,6 +461,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of this script and exit")
+    ap.add_argument("--summarize-launches", metavar="KT_DIR",
+                    help="write profiles/ the launch sequence of one layer step from a rocprofv3 "
+                         "kernel trace of this script (default composition) and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write the MFMA / occupancy counter summary to profiles/ and exit")
     ap.add_argument("--peaks", action="store_true",
@@ -431,10 +478,19 @@ def main():
 
     if args.summarize_counters:
         cmd = ("cd /tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " -d <out>/prof_mfma -o m -f csv -- "
-               "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu")
+               "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --compose split")
         txt = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cmd,
                                  "hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)")
         with open(os.path.join(ROOT, "profiles", "mfma_counters_hybrid.txt"), "w") as f:
+            f.write(txt)
+        print(txt)
+        return
+
+    if args.summarize_launches:
+        txt = summarize_launches(args.summarize_launches,
+                                 "cd /tmp && rocprofv3 --kernel-trace -d <out>/prof_lt -o lt -f csv -- "
+                                 "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu")
+        with open(os.path.join(ROOT, "profiles", "launches_hybrid_default.txt"), "w") as f:
             f.write(txt)
         print(txt)
         return
@@ -444,6 +500,8 @@ def main():
         extra = " --decode %d" % args.decode if args.decode else ""
         title = ("one-token step, %d sequences of the hybrid layer (16/48 heads, d=128)" % args.decode
                  if args.decode else "hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)")
+        # the layer's kernels one launch each (split composition): the roofline's kernel
+        extra = extra or " --compose split"
         cmds = ["cd /tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_kt -o kt -f csv -- "
                 "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu" + extra,
                 "cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/prof_fetch -o f -f csv -- "

@@ -1922,16 +1922,17 @@ bool set_lds_once(Fn fn, size_t lds) {
 
 // Pipelined composition: the scan in chunk-aligned segments (the state carried in
 // `carry`), each launch also running the next segment's prep in workgroups after the
-// scan's own.  Segments are kSegChunks chunks long (the last one may be shorter): on the
-// hybrid layer (512 chunks) 16 segments of 32 measured 0.748 ms, against 0.844 with 8,
-// 0.790 with 12, 0.826 with 32 and 0.922 for the split composition.
-constexpr int kSegChunks = 32;
+// scan's own.  Segments are kSegTokens tokens long (the last one may be shorter): on the
+// hybrid layer (32,768 tokens, chunk 64) 16 segments of 32 chunks measured 0.748 ms,
+// against 0.844 with 8, 0.790 with 12, 0.826 with 32 and 0.922 for the split composition.
+constexpr int kSegTokens = 2048;
 
 template <class Arm, int DK, int C, bool QF32>
 gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int nprep, hipStream_t st) {
+  constexpr int SEG = kSegTokens / C;  // chunks per segment
   const int cps = pl.chunks_per_seq;
-  const int S = (cps + kSegChunks - 1) / kSegChunks;
-  auto cut = [&](int s) { return s < S ? s * kSegChunks : cps; };
+  const int S = (cps + SEG - 1) / SEG;
+  auto cut = [&](int s) { return s < S ? s * SEG : cps; };
   const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
   if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
   using SL = ScanLds<Arm, DK, C, false, QF32, false>;
@@ -1975,7 +1976,8 @@ int pipelined_prep_wgs(const Plan& pl, int nscan) {
   // nothing hides, is too large a share: the single 4,096-token layer, 64 chunks, measured
   // 7 % slower pipelined), an XCD-aligned scan grid, and a prep share of at least a
   // quarter of the scan's
-  if (pl.chunks_per_seq < 4 * kSegChunks || nscan % 8 != 0 || pl.hk % 8 != 0 || nprep < 8 || 4 * nprep < nscan)
+  if ((int64_t)pl.chunks_per_seq * pl.chunk < 4 * kSegTokens || nscan % 8 != 0 || pl.hk % 8 != 0 || nprep < 8 ||
+      4 * nprep < nscan)
     return 0;
   return nprep;
 }

@@ -1,4 +1,4 @@
-"""The pipelined composition (the scan in chunk-aligned segments of 32 chunks carrying
+"""The pipelined composition (the scan in chunk-aligned segments of 2,048 tokens carrying
 the state through the workspace, each segment's launch also running the next segment's
 prep) against the plain split one: every chunk's tiles and every step of the recurrence
 are the same instructions on the same values, and the state crosses a segment boundary
@@ -30,7 +30,7 @@ def _check(inp, arm, o_p, h_p, label):
 @pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_pipelined_bitwise_equals_split(dk, dv, chunk):
-    # 2,500 tokens: 40 chunks of 64 (segments of 32 and 8), 79 chunks of 32 (32, 32, 15)
+    # 2,500 tokens: 40 chunks of 64 (segments of 32 and 8), 79 chunks of 32 (64 and 15)
     spec = inputs.Spec("pipe", (2500, 2500), 2, 6, dk, dv, qkv_dtype="bf16", gate_law="half", h0=True,
                        chunk=chunk, seed=7 * dk + dv + chunk)
     inp = inputs.make(spec)
@@ -109,7 +109,7 @@ def test_library_choice_bitwise_equals_split(cfg):
 
 def test_library_choice_on_this_device():
     """On MI355X (256 compute units) the hybrid layer's scan grid (192 workgroups) leaves
-    64 units idle, so the library pipelines it; the 64-chunk single-sequence layer is
+    64 units idle, so the library pipelines it; the 4,096-token single-sequence layer is
     below the four-segment minimum and stays split."""
     import torch as _t
     if _t.cuda.get_device_properties(0).multi_processor_count < 256:
