@@ -73,8 +73,10 @@ enum { GDN_ARM_MFMA_BF16 = 0, GDN_ARM_FOLD_F32 = 1 };
  * so only the first segment's prep is exposed).  All three give bit-identical results.
  * FUSED is built for the per-head gate with bf16 q/k/v on the bf16 arm; PIPELINED for
  * the per-head gate on fixed-length batches (GDN_E_UNSUPPORTED otherwise); neither has
- * separate stages.  AUTO picks the measured default: pipelined where it applies and the
- * scan grid leaves at least a quarter of its own size idle, else split. */
+ * separate stages.  AUTO picks the measured default: pipelined where it applies, the
+ * sequences are at least four segments (8,192 tokens) long and the scan grid leaves at
+ * least a quarter of its own size idle on the device (gdn_plan_compose reports the
+ * choice), else split. */
 enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2, GDN_COMPOSE_PIPELINED = 3 };
 /* Stages of the split composition a call runs.  0 (or PREP|SCAN) runs both.  A
  * SCAN-only call consumes the chunk tiles a previous PREP call (same problem, same
