@@ -449,11 +449,11 @@ def main():
     ap.add_argument("--config", default="hybrid")
     ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--compose", default="auto", choices=["auto", "split", "fused", "pipelined"],
+    ap.add_argument("--compose", default="auto", choices=["auto", "split", "fused", "pipelined", "seqsplit"],
                     help="auto: the library's choice (gdn_plan_compose says which); split: prep "
                          "kernel then scan (timed per kernel); fused: tile waves inside the scan "
                          "workgroup, one kernel; pipelined: scan segments with the next segment's "
-                         "prep beside each")
+                         "prep beside each; seqsplit: parts of each sequence scanned side by side")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="before each timed step, write this much scratch memory (larger than "
@@ -563,14 +563,14 @@ def main():
     odt_t = torch.bfloat16 if args.arm == "bf16" else torch.float32
     arm = gdn.ARM_MFMA_BF16 if args.arm == "bf16" else gdn.ARM_FOLD_F32
     req = {"auto": gdn.COMPOSE_AUTO, "split": gdn.COMPOSE_SPLIT, "fused": gdn.COMPOSE_FUSED,
-           "pipelined": gdn.COMPOSE_PIPELINED}[args.compose]
+           "pipelined": gdn.COMPOSE_PIPELINED, "seqsplit": gdn.COMPOSE_SEQSPLIT}[args.compose]
     mk = lambda compose, stages: gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else Tn, spec.hk,
                                                   spec.hv, spec.dk, spec.dv, gate, chunk, qdt,
                                                   gdn.BF16 if odt_t == torch.bfloat16 else gdn.F32, arm,
                                                   compose, stages)
     p_all = mk(req, gdn.STAGE_ALL)
     composition = {gdn.COMPOSE_SPLIT: "split", gdn.COMPOSE_FUSED: "fused",
-                   gdn.COMPOSE_PIPELINED: "pipelined"}[gdn.plan_compose(p_all)]
+                   gdn.COMPOSE_PIPELINED: "pipelined", gdn.COMPOSE_SEQSPLIT: "seqsplit"}[gdn.plan_compose(p_all)]
     fused, whole = composition == "fused", composition != "split"
     # the split composition's two stages, called one by one: the per-kernel timing
     p_prep, p_scan = mk(gdn.COMPOSE_SPLIT, gdn.STAGE_PREP), mk(gdn.COMPOSE_SPLIT, gdn.STAGE_SCAN)
@@ -627,7 +627,7 @@ def main():
     scan_v = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ms_step = float(np.median(step_ms))
     prep_ms, scan_ms = float(np.median(prep_v)), float(np.median(scan_v))
-    if composition == "pipelined":
+    if composition in ("pipelined", "seqsplit"):
         # per-kernel times (the roofline's dominant kernel): the split composition's two
         # stages, timed the same way in a second pass of as many cache-cold steps
         step(per_kernel=True)  # untimed: first use of the split kernels' launch attributes
@@ -648,7 +648,7 @@ def main():
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
     log("%s: ms/step %.4f median cold (min %.4f; %sprep %.4f, scan %.4f), warm %.4f, wall %.3f s for %d steps"
-        % (composition, ms_step, step_ms.min(), "split kernels: " if composition == "pipelined" else "",
+        % (composition, ms_step, step_ms.min(), "split kernels: " if composition in ("pipelined", "seqsplit") else "",
            prep_ms, scan_ms, warm_ms, wall, args.steps))
 
     alg = algorithmic(spec, chunk)

@@ -73,11 +73,22 @@ enum { GDN_ARM_MFMA_BF16 = 0, GDN_ARM_FOLD_F32 = 1 };
  * so only the first segment's prep is exposed).  All three give bit-identical results.
  * FUSED is built for the per-head gate with bf16 q/k/v on the bf16 arm; PIPELINED for
  * the per-head gate on fixed-length batches (GDN_E_UNSUPPORTED otherwise); neither has
- * separate stages.  AUTO picks the measured default: pipelined where it applies, the
- * sequences are at least four segments (8,192 tokens) long and the scan grid leaves at
- * least a quarter of its own size idle on the device (gdn_plan_compose reports the
- * choice), else split. */
-enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2, GDN_COMPOSE_PIPELINED = 3 };
+ * separate stages.  AUTO picks the measured default, split or pipelined: pipelined where
+ * it applies, the sequences are at least four segments (8,192 tokens) long and the scan
+ * grid leaves at least a quarter of its own size idle on the device (gdn_plan_compose
+ * reports the choice), else split. */
+enum { GDN_COMPOSE_AUTO = 0, GDN_COMPOSE_SPLIT = 1, GDN_COMPOSE_FUSED = 2, GDN_COMPOSE_PIPELINED = 3,
+       GDN_COMPOSE_SEQSPLIT = 4 };
+/* GDN_COMPOSE_SEQSPLIT, for head-starved shapes (few sequences x heads): each sequence is
+ * cut into 2..4 parts scanned side by side.  Every part scans from zero to its local final
+ * state; each inner part also scans its transition (the product of its chunk maps, a
+ * dk x dk state scanned from the identity with V read as zero); a small kernel chains the
+ * parts' starting states in fp32; the parts after the first then rescan from them with
+ * outputs.  About 1.7x the scan work in two rounds of a part's length instead of one
+ * round of the sequence's.  Per-head gate, fixed-length batches, dk == dv, all stages.
+ * Results equal the other compositions' up to rounding (not bit for bit).  Only on
+ * request: AUTO never picks it (on MI355X it measured slower than split on the
+ * head-starved single-sequence layer it is meant for). */
 /* Stages of the split composition a call runs.  0 (or PREP|SCAN) runs both.  A
  * SCAN-only call consumes the chunk tiles a previous PREP call (same problem, same
  * inputs, same workspace) left in the workspace; the caller orders the two calls,

@@ -27,7 +27,8 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   if (p->o_dtype != GDN_BF16 && p->o_dtype != GDN_F32) return GDN_E_UNSUPPORTED;
   if (p->arm != GDN_ARM_MFMA_BF16 && p->arm != GDN_ARM_FOLD_F32) return GDN_E_UNSUPPORTED;
   if (p->compose != GDN_COMPOSE_AUTO && p->compose != GDN_COMPOSE_SPLIT &&
-      p->compose != GDN_COMPOSE_FUSED && p->compose != GDN_COMPOSE_PIPELINED)
+      p->compose != GDN_COMPOSE_FUSED && p->compose != GDN_COMPOSE_PIPELINED &&
+      p->compose != GDN_COMPOSE_SEQSPLIT)
     return GDN_E_UNSUPPORTED;
   if (p->stages < 0 || p->stages > (GDN_STAGE_PREP | GDN_STAGE_SCAN)) return GDN_E_UNSUPPORTED;
   // the fused composition (tile waves inside the scan workgroup) is built for the
@@ -42,6 +43,10 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   const bool pipe_ok = p->gate == GDN_GATE_HEAD && p->seq_len > 0 &&
                        (p->stages == GDN_STAGE_ALL || p->stages == (GDN_STAGE_PREP | GDN_STAGE_SCAN));
   if (p->compose == GDN_COMPOSE_PIPELINED && !pipe_ok) return GDN_E_UNSUPPORTED;
+  // the sequence split (parts scanned side by side, chained through their transitions)
+  // additionally needs square states: a transition is a dk x dk state scanned like a value
+  const bool seq_ok = pipe_ok && p->dk == p->dv;
+  if (p->compose == GDN_COMPOSE_SEQSPLIT && !seq_ok) return GDN_E_UNSUPPORTED;
   Plan pl;
   memset(&pl, 0, sizeof(pl));
   pl.n_seq = p->n_seq;
@@ -59,6 +64,9 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   pl.fused = p->compose == GDN_COMPOSE_FUSED;
   pl.pipe_ok = pipe_ok && (p->compose == GDN_COMPOSE_AUTO || p->compose == GDN_COMPOSE_PIPELINED);
   pl.pipe_req = p->compose == GDN_COMPOSE_PIPELINED ? 1 : (p->compose == GDN_COMPOSE_AUTO ? -1 : 0);
+  // (only on request: measured slower than split on the shapes it is for, see seqsplit_parts)
+  pl.seq_ok = seq_ok && p->compose == GDN_COMPOSE_SEQSPLIT;
+  pl.seq_req = p->compose == GDN_COMPOSE_SEQSPLIT ? 1 : 0;
   pl.run_prep = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_PREP);
   pl.run_scan = p->stages == GDN_STAGE_ALL || (p->stages & GDN_STAGE_SCAN);
   // The fixed-length form is chosen when seq_len > 0 or when there are no tokens at all;
@@ -107,6 +115,10 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   const size_t carry = pl.pipe_ok ? (size_t)pl.n_seq * pl.hv * pl.dk * pl.dv * 4 : 0;
   pl.off_carry = off;
   off = round_up(off + carry, 256);
+  // sequence split: per-part states, transitions and chained inputs (up to kMaxParts parts)
+  const size_t parts = pl.seq_ok ? 3 * (size_t)kMaxParts * pl.n_seq * pl.hv * pl.dk * pl.dv * 4 : 0;
+  pl.off_parts = off;
+  off = round_up(off + parts, 256);
   pl.bytes = off;
   *out = pl;
   return GDN_OK;
@@ -224,6 +236,12 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   prm.prep_ce = prm.seg_ce;
   prm.nscan = (int32_t)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
   prm.h0_input = 1;
+  if (ws && pl.seq_ok) {
+    const size_t one = (size_t)gdn::kMaxParts * pl.n_seq * pl.hv * pl.dk * pl.dv;
+    prm.Bws = (float*)(ws + pl.off_parts);
+    prm.Mws = prm.Bws + one;
+    prm.Hws = prm.Mws + one;
+  }
   return gdn::launch(pl, prm, ws ? ws + pl.off_carry : nullptr, stream);
 }
 

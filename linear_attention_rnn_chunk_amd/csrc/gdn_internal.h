@@ -19,6 +19,9 @@ constexpr int tile_frag_index(int mt, int sb) {
 constexpr int tile_frags(int C) { return tile_frag_index(C / 16, 0); }
 constexpr int tile_elems(int C) { return tile_frags(C) * 512; }
 
+// Most parts the sequence-split composition cuts a sequence into.
+constexpr int kMaxParts = 4;
+
 // Everything a launch needs, resolved on the host from a gdn_problem.
 struct Plan {
   int32_t n_seq, seq_len, hk, hv, dk, dv;
@@ -31,13 +34,16 @@ struct Plan {
   int32_t pipe_ok;       // pipelined composition possible and not excluded by the request
                          // (per-head gate, fixed length, all stages, AUTO or PIPELINED)
   int32_t pipe_req;      // 1: pipelined requested, 0: split requested, -1: library choice
+  int32_t seq_ok;        // sequence-split composition requested and possible
+                         // (per-head gate, fixed length, dk == dv, all stages)
+  int32_t seq_req;       // 1: sequence split requested, 0: not
   int32_t run_prep, run_scan;  // stages to launch
   int32_t varlen;        // 1: cu_seqlens given
   int32_t chunks_per_seq;  // fixed-length batches
   int64_t max_slots;     // chunk slots the prep grid covers
   // workspace carve-up (byte offsets)
   int32_t kq_ws;         // 1: K and Q copied to the workspace in the arm's type
-  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, off_carry, bytes;
+  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, off_carry, off_parts, bytes;
 };
 
 // Kernel arguments (by value).
@@ -69,6 +75,18 @@ struct Params {
   // [prep_cb, prep_ce).  Scan workgroups are blockIdx < nscan; in the pipelined
   // composition the workgroups after them run the prep of the next segment.
   int32_t seg_cb, seg_ce, prep_cb, prep_ce, nscan, h0_input;
+  // Sequence-split composition (fixed-length batches, dk == dv).  pmode 0: off.  Else each
+  // sequence is cut into nparts parts of part_chunks chunks, and the launch's "sequences"
+  // are pvirt virtual ones per real sequence.  pmode 1: virtual v < nparts scans part v from
+  // h0 (v = 0) or zero, writes its outputs and leaves its state in Bws; v >= nparts scans
+  // part v - nparts + 1 from the identity with V read as zero and no outputs, leaving the
+  // part's transition in Mws.  pmode 2: virtual v scans part v + 1 from Hws, writes its
+  // outputs, and the last part writes hT; part 1 starts from Bws part 0, later parts from
+  // Hws.  Bws, Mws, Hws: [n_seq][nparts][hv][dk][dv] fp32.
+  int32_t pmode, nparts, pvirt, part_chunks;
+  float* Bws;
+  float* Mws;
+  float* Hws;
 };
 
 // Arguments of the one-token recurrent step (by value).

@@ -1310,17 +1310,37 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   }
   const int kh = h / (p.hv / p.hk);
 
+  // Sequence split: virtual sequence n is part `part` of real sequence nr; kind 0 scans the
+  // part's own state, kind 1 its transition (identity start, V read as zero, no outputs),
+  // kind 2 rescans it from its chained starting state.
+  // (built only where it applies: per-head gate, split kernels)
+  constexpr bool PARTS = !KDA && !FUSED;
+  int nr = n, part = 0, kind = 0;
+  if (PARTS && p.pmode) {
+    nr = n / p.pvirt;
+    const int v = n - nr * p.pvirt;
+    if (p.pmode == 1) {
+      part = v < p.nparts ? v : v - p.nparts + 1;
+      kind = v < p.nparts ? 0 : 1;
+    } else {
+      part = v + 1;
+      kind = 2;
+    }
+  }
   int64_t s0, s1, slot0;
   if (p.varlen) {
     s0 = p.table[n];
     s1 = p.table[n + 1];
     slot0 = p.table[p.n_seq + 1 + n];
-  } else {  // this launch's chunks [seg_cb, seg_ce) of the sequence
-    const int64_t b = (int64_t)n * p.seq_len;
-    s0 = b + min64(p.seq_len, (int64_t)p.seg_cb * C);
-    s1 = b + min64(p.seq_len, (int64_t)p.seg_ce * C);
-    slot0 = (int64_t)n * p.chunks_per_seq + p.seg_cb;
+  } else {  // this launch's chunks [cb, ce) of the sequence (a segment, a part or all)
+    const int cb = PARTS && p.pmode ? part * p.part_chunks : p.seg_cb;
+    const int ce = PARTS && p.pmode ? (part + 1) * p.part_chunks : p.seg_ce;
+    const int64_t b = (int64_t)nr * p.seq_len;
+    s0 = b + min64(p.seq_len, (int64_t)cb * C);
+    s1 = b + min64(p.seq_len, (int64_t)ce * C);
+    slot0 = (int64_t)nr * p.chunks_per_seq + cb;
   }
+  const bool vzero = PARTS && kind == 1, no_out = PARTS && kind == 1;
   const int nch = (int)((s1 - s0 + C - 1) / C);
   uint32_t bad = 0;
 
@@ -1584,7 +1604,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) nf |= (__float_as_uint(o[u][nt][j]) & 0x7F800000u) + 0x00800000u;
-      bad |= flag_if(nf & 0x80000000u, GDN_ST_NONFINITE_OUTPUT);
+      bad |= flag_if(!no_out && (nf & 0x80000000u), GDN_ST_NONFINITE_OUTPUT);
       // rows of this chunk: uniform base plus the lane's fixed row offsets
       char* ob = (char*)p.o + ((t0 * hvs + h) * (int64_t)DV + 32 * slice) * OSZ;
       // lane (i, g) of tile nt holds row 16 nt + i, slice columns 8 g .. 8 g + 7 (the
@@ -1600,7 +1620,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           *(u32x4*)a = (u32x4){w0.x, w0.y, w1.x, w1.y};
         }
       };
-      if (L == C) {
+      if (no_out) {
+      } else if (L == C) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st(nt);
       } else {
@@ -1642,19 +1663,33 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // quads, so the output wave holds 8 consecutive columns of a row per lane
     const int ccol = 8 * (i >> 2) + 4 * u + (i & 3);
     const int col0 = 32 * slice + ccol;
-    const int64_t hbase = ((int64_t)n * p.hv + h) * DK * (int64_t)DV;
+    // this workgroup's starting state and where its final state goes ([dk][dv] fp32 each)
+    const int64_t hsz = DK * (int64_t)DV, hbase = ((int64_t)n * p.hv + h) * hsz;
+    const float* hin = p.h0 ? p.h0 + hbase : nullptr;
+    float* hout = p.hT ? p.hT + hbase : nullptr;
+    bool hcheck = p.h0_input;
+    if (PARTS && p.pmode) {
+      const int64_t real = ((int64_t)nr * p.hv + h) * hsz, pt = (((int64_t)nr * p.nparts + part) * p.hv + h) * hsz;
+      // (the second part starts from the first part's own final state)
+      const float* h2 = part == 1 ? p.Bws + (((int64_t)nr * p.nparts) * p.hv + h) * hsz : p.Hws + pt;
+      hin = kind == 0 ? (part == 0 && p.h0 ? p.h0 + real : nullptr) : (kind == 2 ? h2 : nullptr);
+      hout = kind == 0 ? p.Bws + pt : (kind == 1 ? p.Mws + pt : (part == p.nparts - 1 && p.hT ? p.hT + real : nullptr));
+      hcheck = kind == 0 && part == 0;
+    }
     f32x4 H[NTK];
-    if (p.h0) {
+    if (hin) {
 #pragma unroll
       for (int t = 0; t < NTK; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          H[t][j] = p.h0[hbase + (int64_t)state_dim(t, g, j) * DV + col0];
-          bad |= flag_if(p.h0_input && f_nonfinite(H[t][j]), GDN_ST_NONFINITE_INPUT);
+          H[t][j] = hin[(int64_t)state_dim(t, g, j) * DV + col0];
+          bad |= flag_if(hcheck && f_nonfinite(H[t][j]), GDN_ST_NONFINITE_INPUT);
         }
     } else {
 #pragma unroll
-      for (int t = 0; t < NTK; ++t) H[t] = zero4();
+      for (int t = 0; t < NTK; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) H[t][j] = (PARTS && kind == 1 && state_dim(t, g, j) == col0) ? 1.f : 0.f;
     }
     F HB[NBK];
 #pragma unroll
@@ -1714,6 +1749,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           const int r = 16 * mt + 4 * g + j;
           if constexpr (QF32) vv[mt][j] = *(const float*)(B + SL::VV + (r * 32 + ccol) * 4);
           else vv[mt][j] = bf2f(*(const uint16_t*)(B + SL::VV + (r * 32 + ccol) * 2));
+          if (vzero) vv[mt][j] = 0.f;
         }
       float4 b4[NT], e4[NT];
 #pragma unroll
@@ -1839,13 +1875,13 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       cstep(std::integral_constant<int, 1>{}, ci + 1);
     }
     if (ci < nch) cstep(std::integral_constant<int, 0>{}, ci);
-    if (p.hT) {
+    if (hout) {
 #pragma unroll
       for (int t = 0; t < NTK; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           bad |= flag_if(f_nonfinite(H[t][j]), GDN_ST_NONFINITE_OUTPUT);
-          p.hT[hbase + (int64_t)state_dim(t, g, j) * DV + col0] = H[t][j];
+          hout[(int64_t)state_dim(t, g, j) * DV + col0] = H[t][j];
         }
     }
   } else if constexpr (FUSED) {
@@ -1900,6 +1936,41 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     for (; passed < nch + 1; ++passed) __syncthreads();
   }
   if (bad) atomicOr(p.status, bad);
+}
+
+// Sequence split: one step of the chain of the parts' starting states, in fp32 from the
+// parts' own final states B (scanned from zero) and transitions M (scanned from the
+// identity with V read as zero): H_{q+1} = M_q H_q + B_q, with H_1 = B_0.  One workgroup
+// per (sequence, value head, 32 state columns, 32 rows of the result); the 32 columns of
+// H_q and the 32 rows of M_q are staged in LDS; fixed summation order.
+__global__ __launch_bounds__(256) void gdn_seq_chain(Params p, int DK, int q) {
+  __shared__ float Hs[128][33];
+  __shared__ float Ms[32][129];
+  const int DV = p.dv, ns = DV / 32, nr = DK / 32;
+  int b = (int)blockIdx.x;
+  const int rb = b % nr;
+  b /= nr;
+  const int slice = b % ns;
+  b /= ns;
+  const int h = b % p.hv, n = b / p.hv;
+  const int t = threadIdx.x, c = t & 31, r0 = t >> 5;  // column; rows r0 + 8 k of the block
+  const int64_t hsz = (int64_t)DK * DV;
+  auto at = [&](float* base, int part) { return base + (((int64_t)n * p.nparts + part) * p.hv + h) * hsz; };
+  const float* Hq = q == 1 ? at(p.Bws, 0) : at(p.Hws, q);
+  const float* M = at(p.Mws, q);
+  for (int i = r0; i < DK; i += 8) Hs[i][c] = Hq[(int64_t)i * DV + 32 * slice + c];
+  for (int e = t; e < 32 * DK; e += 256) Ms[e / DK][e % DK] = M[(int64_t)(32 * rb + e / DK) * DK + e % DK];
+  __syncthreads();
+  const float* Bq = at(p.Bws, q);
+  float* out = at(p.Hws, q + 1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = r0 + 8 * k, i = 32 * rb + rr;
+    const int64_t e = (int64_t)i * DV + 32 * slice + c;
+    float acc = Bq[e];
+    for (int j = 0; j < DK; ++j) acc = fmaf(Ms[rr][j], Hs[j][c], acc);
+    out[e] = acc;
+  }
 }
 
 // ------------------------------------------------------------ launch -----
@@ -1982,12 +2053,60 @@ int pipelined_prep_wgs(const Plan& pl, int nscan) {
   return nprep;
 }
 
+// Parts the sequence-split composition cuts each sequence into: the most (up to kMaxParts)
+// whose first launch -- every part's own scan plus the inner parts' transitions, 2 P - 2
+// scan grids -- fits the device in one round; 0 when it was not requested.  The library
+// never picks it itself: on the single-sequence layer (4,096 tokens, 16 heads, 64 scan
+// workgroups) three parts measured 0.106 ms against 0.099 ms split, because the scan's
+// step slows as the grid grows (1.5 us a step at 256 workgroups against 1.17 at 64) and
+// the extra launches and the chain take the rest of the saving.
+int seqsplit_parts(const Plan& pl, int nscan) {
+  if (!pl.seq_ok || pl.seq_req != 1 || nscan <= 0) return 0;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 0;
+  int parts = ncu / (2 * nscan) + 1;
+  if (parts > kMaxParts) parts = kMaxParts;
+  return parts < 2 ? 2 : parts;
+}
+
+template <class Arm, int DK, int C, bool QF32>
+gdn_status run_seqsplit(const Plan& pl, const Params& prm, int parts, hipStream_t st) {
+  const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
+  if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
+  using SL = ScanLds<Arm, DK, C, false, QF32, false>;
+  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false>, SL::BYTES)) return GDN_E_LAUNCH;
+  hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)((pl.max_slots + 7) / 8 * 8 * pl.hk * nblk)),
+                     dim3(64 * wpb), wpb * SolveLds<C>::FLOATS * sizeof(float), st, prm);
+  if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
+  const int per = pl.hv * (pl.dv / 32);  // scan workgroups per (virtual) sequence
+  Params q = prm;
+  q.pmode = 1;
+  q.nparts = parts;
+  q.part_chunks = (pl.chunks_per_seq + parts - 1) / parts;
+  q.pvirt = 2 * parts - 2;  // every part's own state, the inner parts' transitions
+  q.nscan = pl.n_seq * q.pvirt * per;
+  hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false>), dim3((unsigned)q.nscan), dim3(256), SL::BYTES, st, q);
+  if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
+  for (int step = 1; step + 1 < parts; ++step) {  // chain: H_{step+1} = M_step H_step + B_step
+    hipLaunchKernelGGL(gdn_seq_chain, dim3((unsigned)(pl.n_seq * per * (DK / 32))), dim3(256), 0, st, q, DK, step);
+    if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
+  }
+  q.pmode = 2;
+  q.pvirt = parts - 1;  // the parts after the first, from their chained states
+  q.nscan = pl.n_seq * q.pvirt * per;
+  hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false>), dim3((unsigned)q.nscan), dim3(256), SL::BYTES, st, q);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_E_LAUNCH;
+}
+
 template <class Arm, int DK, int C, bool KDA, bool QF32>
 gdn_status run(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
-  if constexpr (!KDA) {  // the same decision as plan_compose()
+  if constexpr (!KDA) {  // the same decisions as plan_compose()
     const int nprep = pipelined_prep_wgs(pl, prm.nscan);
     if (nprep > 0 && pl.run_prep && pl.run_scan && pl.max_slots > 0)
       return run_pipelined<Arm, DK, C, QF32>(pl, prm, (float*)carry, nprep, st);
+    const int parts = seqsplit_parts(pl, prm.nscan);
+    if (parts > 0 && pl.run_prep && pl.run_scan && pl.max_slots > 0) return run_seqsplit<Arm, DK, C, QF32>(pl, prm, parts, st);
   }
   if (pl.run_prep && !pl.fused && pl.max_slots > 0) {
     if constexpr (KDA) {
@@ -2055,6 +2174,8 @@ int32_t plan_compose(const Plan& pl) {
   const int nscan = (int)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
   if (!pl.gate_channel && pl.run_prep && pl.run_scan && pl.max_slots > 0 && pipelined_prep_wgs(pl, nscan) > 0)
     return GDN_COMPOSE_PIPELINED;
+  if (!pl.gate_channel && pl.run_prep && pl.run_scan && pl.max_slots > 0 && seqsplit_parts(pl, nscan) > 0)
+    return GDN_COMPOSE_SEQSPLIT;
   return GDN_COMPOSE_SPLIT;
 }
 

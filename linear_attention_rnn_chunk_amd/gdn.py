@@ -25,7 +25,7 @@ ST_NONFINITE_OUTPUT = 0x8
 GATE_HEAD, GATE_KEY_CHANNEL = 0, 1
 BF16, F32 = 0, 1
 ARM_MFMA_BF16, ARM_FOLD_F32 = 0, 1
-COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED, COMPOSE_PIPELINED = 0, 1, 2, 3
+COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED, COMPOSE_PIPELINED, COMPOSE_SEQSPLIT = 0, 1, 2, 3, 4
 STAGE_ALL, STAGE_PREP, STAGE_SCAN = 0, 1, 2
 
 # every symbol include/gdn.h declares
@@ -140,7 +140,7 @@ def _ptr(t: Optional[torch.Tensor]):
 _DT = {torch.bfloat16: BF16, torch.float32: F32}
 _ARM = {"bf16": ARM_MFMA_BF16, "f32": ARM_FOLD_F32}
 _COMPOSE = {"auto": COMPOSE_AUTO, "split": COMPOSE_SPLIT, "fused": COMPOSE_FUSED,
-            "pipelined": COMPOSE_PIPELINED}
+            "pipelined": COMPOSE_PIPELINED, "seqsplit": COMPOSE_SEQSPLIT}
 
 
 def chunk_fwd_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT, status, workspace,

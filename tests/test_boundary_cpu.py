@@ -80,6 +80,13 @@ def P(**kw):
     (dict(compose=gdn.COMPOSE_PIPELINED, gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=gdn.COMPOSE_PIPELINED, n_seq=3, seq_len=0), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=gdn.COMPOSE_PIPELINED, stages=gdn.STAGE_SCAN), gdn.GDN_E_UNSUPPORTED),
+    # the sequence split: as pipelined, and square states (dk == dv)
+    (dict(compose=gdn.COMPOSE_SEQSPLIT), gdn.GDN_OK),
+    (dict(compose=gdn.COMPOSE_SEQSPLIT, dk=64, dv=64), gdn.GDN_OK),
+    (dict(compose=gdn.COMPOSE_SEQSPLIT, dk=128, dv=64), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_SEQSPLIT, gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_SEQSPLIT, n_seq=3, seq_len=0), gdn.GDN_E_UNSUPPORTED),
+    (dict(compose=gdn.COMPOSE_SEQSPLIT, stages=gdn.STAGE_PREP), gdn.GDN_E_UNSUPPORTED),
 ])
 def test_validate_refusals(kw, code):
     assert gdn.validate(P(**kw)) == code
@@ -90,6 +97,7 @@ def test_plan_compose_host_rules():
     # AUTO resolves to split or pipelined (the latter only where the device has idle units)
     assert gdn.plan_compose(P(compose=gdn.COMPOSE_SPLIT)) == gdn.COMPOSE_SPLIT
     assert gdn.plan_compose(P(compose=gdn.COMPOSE_FUSED)) == gdn.COMPOSE_FUSED
+    assert gdn.plan_compose(P(compose=gdn.COMPOSE_SEQSPLIT)) == gdn.COMPOSE_SEQSPLIT
     assert gdn.plan_compose(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32)) == gdn.COMPOSE_SPLIT
     assert gdn.plan_compose(P(n_seq=3, seq_len=0)) == gdn.COMPOSE_SPLIT
     assert gdn.plan_compose(P(compose=gdn.COMPOSE_AUTO)) in (gdn.COMPOSE_SPLIT, gdn.COMPOSE_PIPELINED)
@@ -121,9 +129,14 @@ def test_workspace_bytes_scales_with_tiles():
         assert 2 * s * hv * elems * 4 + kq <= f32 < 2 * s * hv * elems * 4 + kq + 1024
     # the library's choice may pipeline a fixed-length per-head-gate batch: the state
     # carried between scan segments, [n_seq][hv][dk][dv] fp32, on top of the split tiles
+    # the sequence split (on request only): per-part states, transitions and chained
+    # inputs, 3 x 4 parts of [n_seq][hv][dk][dv] fp32
     carry = 1 * hv * 128 * 128 * 4
+    parts = 3 * 4 * carry
     assert gdn.workspace_bytes(P()) == gdn.workspace_bytes(P(compose=gdn.COMPOSE_SPLIT)) + carry
     assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_PIPELINED)) == gdn.workspace_bytes(P())
+    assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_SEQSPLIT)) == \
+        gdn.workspace_bytes(P(compose=gdn.COMPOSE_SPLIT)) + parts
     assert gdn.workspace_bytes(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32)) == \
         gdn.workspace_bytes(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32, compose=gdn.COMPOSE_SPLIT))
     # fused composition: no tiles in the workspace (only the chunk table of a packed batch)
