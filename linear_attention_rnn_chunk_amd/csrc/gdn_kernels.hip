@@ -820,8 +820,9 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
 }
 
 // The prep of the next scan segment, run by the workgroups of a pipelined scan launch
-// after the scan's own (blockIdx >= nscan, a multiple of 8, so these workgroups too sit
-// on XCD blockIdx % 8).  They stay resident and loop: wave w of prep workgroup b takes
+// after the scan's own (blockIdx >= nscan; the library's choice requires nscan to be a
+// multiple of 8, so these workgroups too sit on XCD blockIdx % 8 -- otherwise only the
+// L2 sharing below is lost).  They stay resident and loop: wave w of prep workgroup b takes
 // units (slot of the range, key head), key head fastest, among the slots m = x, x + 8,
 // ... that belong to its XCD x, with a stride of all the XCD's prep waves.  A unit loads
 // K and Q and forms K K^T and Q K^T once, then gates, solves and stores the tiles of each
