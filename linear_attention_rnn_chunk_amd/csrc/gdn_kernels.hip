@@ -21,7 +21,12 @@
 //                    T and P for every value head of the group
 //   gdn_scan         one workgroup per (sequence, value head, 32 state columns), one
 //                    wave per 16 columns; fp32 state lives in MFMA accumulators and
-//                    never leaves registers; walks the chunks serially
+//                    never leaves registers; walks the chunks serially.  It also runs
+//                    any chunk range of each sequence from and to given state buffers
+//                    (the pipelined composition's segments, whose launches run the next
+//                    segment's prep in workgroups after the scan's own) and the parts of
+//                    the sequence-split composition (own state, transition, rescan)
+//   gdn_seq_chain    sequence split: one fp32 step of the chain of the parts' states
 //
 // MFMA fragment convention (16x16 tiles, K = 32 per fragment): lane l holds column
 // (or row) l%16 and, with g = l/16, the contraction positions {4g..4g+3} and
@@ -1073,7 +1078,8 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
 //               ci + NBUF - 1 global -> LDS directly (no register round trip) into a ring
 //               of NBUF chunk buffers, runs the in-chunk gate sweep ahead, checks V
 // One workgroup barrier per chunk.  The fused composition adds two tile waves that form T
-// and P in the workgroup (described with their code below).
+// and P in the workgroup (described with their code below).  In a pipelined launch the
+// workgroups past the scan's (blockIdx >= nscan) are prep workgroups (prep_role).
 //
 // State rows are stored permuted within each 32-key block: accumulator tile t = 2 kb + h,
 // row 4 g + j holds key dim pi = 32 kb + 8 g + 4 h + j.  Two stacked accumulator tiles are
