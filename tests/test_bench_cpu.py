@@ -1,5 +1,6 @@
 """The benchmark's algorithmic byte and flop counts (the numerators of its roofline
-fractions), checked on the CPU against counts made independently of its formulas."""
+fractions), checked on the CPU against counts made independently of its formulas; and
+its summary of a per-launch kernel trace."""
 import os
 import sys
 
@@ -45,3 +46,45 @@ def test_decode_bytes():
     n = bench.decode_bytes(256, 16, 48, 128, 128)
     assert n == 256 * 48 * (2 * 128 * 128 * 4 + 2 * 128 * 2 + 8) + 256 * 16 * 2 * 128 * 2
     assert n == 1_619_099_648
+
+
+def test_launch_summary_picks_a_timed_step(tmp_path):
+    """summarize_launches reads a per-dispatch kernel trace, cuts it into steps at the
+    non-library kernels (the cache flush before each timed step) and shows one of the
+    most common step shape: warm-up steps (back to back, merged) and the two-launch
+    per-kernel pass are not taken for it."""
+    import csv
+    import bench
+    d = tmp_path / "kt"
+    d.mkdir()
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X"]
+    rows, t = [], 0
+
+    def k(name, dur, wg):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur,
+                     "Workgroup_Size_X": 256, "Grid_Size_X": 256 * wg})
+        t += dur + 10
+
+    step = [("gdn_prep_head<x>", 20000, 512)] + [("gdn_scan<x>", 48000, 256)] * 3 + [("gdn_scan<x>", 43000, 192)]
+    for _ in range(3):  # warm-up: back to back
+        for s in step:
+            k(*s)
+    for _ in range(5):  # timed: a flush before each
+        k("at::native::fill", 140000, 4096)
+        for s in step:
+            k(*s)
+    for _ in range(4):  # per-kernel pass: two launches a step
+        k("at::native::fill", 140000, 4096)
+        k("gdn_prep_head<x>", 150000, 8192)
+        k("gdn_scan<x>", 770000, 192)
+    with open(d / "x_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+    txt = bench.summarize_launches(str(d), "cmd")
+    assert "timed steps of 5 launches in the trace: 5" in txt
+    lines = [l for l in txt.splitlines() if l.startswith("gdn_")]
+    assert lines == ["gdn_prep_head  512  20.0", "gdn_scan  256  48.0", "gdn_scan  256  48.0",
+                     "gdn_scan  256  48.0", "gdn_scan  192  43.0"]
+    assert "span_us: 207.0" in txt
