@@ -56,7 +56,8 @@ def algorithmic(spec, chunk):
     # fragments of a 64 x 64 tile, both of a 32 x 32 tile
     tile = sum(mt // 2 + 1 for mt in range(chunk // 16)) * 512 * esz
     qk = 2 * T * hk * dk * 2
-    gb = 2 * T * hv * 4
+    # gate (per head [T][hv], or per key channel [T][hv][dk]) and beta, fp32
+    gb = T * hv * (dk if spec.gate == "channel" else 1) * 4 + T * hv * 4
     prep_bytes = qk + gb + 2 * nch * hv * tile
     prep_flops = nch * hk * 2 * chunk * chunk * dk + nch * hv * chunk ** 3 / 3
     state = 2 * n_seq * hv * dk * dv * 4 if spec.h0 else n_seq * hv * dk * dv * 4
@@ -66,6 +67,30 @@ def algorithmic(spec, chunk):
     layer_bytes = qk + gb + 2 * T * hv * dv * 2 + state
     return dict(prep_bytes=prep_bytes, prep_flops=prep_flops, scan_bytes=scan_bytes,
                 scan_flops=scan_flops, chunks=nch, layer_bytes=layer_bytes)
+
+
+def scope_flops(spec, chunk):
+    """Algorithmic flops of one layer as the hot-path scope table counts them, per chunk of
+    C tokens: 2 C^2 dk per key head (K K^T strictly lower + Q K^T lower), and per value head
+    C^3 / 3 (triangular inverse) + C^2 (dk + dv) (the W and U' folds) + 4 C dk dv (state
+    update) + 2 C dk dv + C^2 dv (output).  Partial chunks count as whole ones."""
+    nch = sum((l + chunk - 1) // chunk for l in spec.seq_lens)
+    C, dk, dv = chunk, spec.dk, spec.dv
+    per_kh = 2 * C * C * dk
+    per_hv = C ** 3 / 3 + C * C * (dk + dv) + 4 * C * dk * dv + 2 * C * dk * dv + C * C * dv
+    return nch * spec.hk * per_kh + nch * spec.hv * per_hv
+
+
+def composition_overhead_bytes(spec, chunk):
+    """HBM bytes the split-type compositions move on top of the compulsory ones: every
+    chunk's T and P fragments written by the prep and read back by the scan (per-channel
+    gate: also the gated operands e^G K, e^{G_C - G} K, e^G Q and the chunk decay)."""
+    nch = sum((l + chunk - 1) // chunk for l in spec.seq_lens)
+    tile = sum(mt // 2 + 1 for mt in range(chunk // 16)) * 512 * 2
+    per = 2 * tile
+    if spec.gate == "channel":
+        per += 3 * chunk * spec.dk * 2 + spec.dk * 4
+    return 2 * nch * spec.hv * per
 
 
 # the source file holding each workload's kernels and their launch code
@@ -83,25 +108,38 @@ def source_digest(label="hybrid"):
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel, digest, label="hybrid"):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if it was
-    taken on the current kernel source (same digest); else None."""
+def traffic_from_profiles(label, composition, digest, kernel=None):
+    """HBM bytes from the committed counter summary of workload `label`, if it was taken on
+    the current kernel source (same digest) and the same composition; else None.  Without
+    `kernel`: the bytes of one whole call (every launch of one step); with it, that
+    kernel's bytes per launch."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % label)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m = re.search(r"source_digest:\s*(\w+)", txt)
-    if not m or m.group(1) != digest:
+    c = re.search(r"composition:\s*(\w+)", txt)
+    if not m or m.group(1) != digest or not c or c.group(1) != composition:
         return None
-    m = re.search(r"^%s\s+bytes_per_launch:\s*([0-9.eE+]+)" % re.escape(kernel), txt, re.M)
+    key = r"%s\s+bytes_per_launch" % re.escape(kernel) if kernel else "bytes_per_step"
+    m = re.search(r"^%s:\s*([0-9.eE+]+)" % key, txt, re.M)
     return float(m.group(1)) if m else None
 
 
-def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds, label="hybrid",
-                       title="hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)"):
-    """Text summaries of rocprofv3 runs of this script: kernel durations (kernel trace) and
-    HBM bytes per launch (FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same
-    counter reads for the plain copy of --copy-probe, whose true bytes are known)."""
+def _short_kernel(name):
+    m = re.search(r"(gdn_\w+)<", name) or re.search(r"(gdn_\w+)\(", name) or re.search(r"(gdn_\w+)", name)
+    if m:
+        return m.group(1)
+    if "AUnaryFunctor" in name or "MulFunctor" in name:
+        return "copy_probe"
+    return None
+
+
+def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds, label, composition, calls, title):
+    """Text summaries of rocprofv3 runs of this script (each making `calls` whole layer
+    calls): kernel durations (kernel trace: per kernel, and their sum per call), and HBM
+    bytes per launch and per call (FETCH_SIZE and WRITE_SIZE passes, each scaled by what
+    the same counter reads for the plain copy of --copy-probe, whose true bytes are known)."""
     import csv
     import glob
     import numpy as np
@@ -112,53 +150,56 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, cmds, label="hybrid",
             out += list(csv.DictReader(open(f)))
         return out
 
-    def short(name):
-        m = re.search(r"(gdn_\w+)<", name) or re.search(r"(gdn_\w+)\(", name)
-        if m:
-            return m.group(1)
-        if "AUnaryFunctor" in name or "MulFunctor" in name:
-            return "copy_probe"
-        return None
-
     kt = rows(kt_dir, "*kernel_stats.csv")
     lines = ["# rocprofv3 kernel trace: " + title,
-             "# command: " + cmds[0], "kernel  calls  avg_us  min_us  max_us  share_pct"]
+             "# command: " + cmds[0],
+             "composition: %s" % composition,
+             "kernel  calls  avg_us  min_us  max_us  share_pct"]
+    total_ns = 0.0
     for r in kt:
-        k = short(r["Name"])
+        k = _short_kernel(r["Name"])
         if k and k != "copy_probe":
+            total_ns += float(r["TotalDurationNs"]) if "TotalDurationNs" in r else float(r["AverageNs"]) * int(r["Calls"])
             lines.append("%s  %s  %.2f  %.2f  %.2f  %s" % (k, r["Calls"], float(r["AverageNs"]) / 1e3,
                                                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
                                                         r["Percentage"]))
+    lines.append("kernel_us_per_call: %.2f  (sum of the gdn kernels' durations / %d calls)" % (total_ns / 1e3 / calls, calls))
     trace_txt = "\n".join(lines) + "\n"
 
     per = {}
     for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         for r in rows(d, "*counter_collection.csv"):
-            k = short(r["Kernel_Name"])
+            k = _short_kernel(r["Kernel_Name"])
             if k and r["Counter_Name"] == cname:
                 per.setdefault((k, cname), []).append(float(r["Counter_Value"]))
     probe_kib = PROBE_MIB * 1024.0
     f_scale = probe_kib / np.mean(per[("copy_probe", "FETCH_SIZE")])
     w_scale = probe_kib / np.mean(per[("copy_probe", "WRITE_SIZE")])
-    lines = ["# HBM traffic per launch from rocprofv3 counters: " + title,
+    lines = ["# HBM traffic from rocprofv3 counters: " + title,
              "# commands: " + cmds[1], "#           " + cmds[2],
              "# copy probe: %d MiB read and written; FETCH_SIZE read %.1f KiB (scale %.4f), "
              "WRITE_SIZE %.1f KiB (scale %.4f)" % (PROBE_MIB, np.mean(per[("copy_probe", "FETCH_SIZE")]),
                                                   f_scale, np.mean(per[("copy_probe", "WRITE_SIZE")]), w_scale),
+             "composition: %s" % composition,
              "source_digest: %s" % source_digest(label)]
+    step = 0.0
     for k in sorted({k for k, _ in per if k != "copy_probe"}):
         fk = np.mean(per[(k, "FETCH_SIZE")]) * f_scale
         wk = np.mean(per[(k, "WRITE_SIZE")]) * w_scale
+        n = len(per[(k, "FETCH_SIZE")])
+        step += (np.sum(per[(k, "FETCH_SIZE")]) * f_scale + np.sum(per[(k, "WRITE_SIZE")]) * w_scale) * 1024 / calls
+        lines.append("%s launches: %d (%.3g per call)" % (k, n, n / calls))
         lines.append("%s fetch_bytes: %.6g" % (k, fk * 1024))
         lines.append("%s write_bytes: %.6g" % (k, wk * 1024))
         lines.append("%s bytes_per_launch: %.6g" % (k, (fk + wk) * 1024))
+    lines.append("bytes_per_step: %.6g  (every gdn launch of one call)" % step)
     return trace_txt, "\n".join(lines) + "\n"
 
 
-def summarize_launches(kt_dir, cmd):
-    """The launches of one step of the default composition (the last timed step before the
-    per-kernel pass), from a per-dispatch kernel trace: each gdn kernel's duration and
-    workgroups, and the span from the first launch's start to the last one's end."""
+def summarize_launches(kt_dir, cmd, title, composition):
+    """The launches of one cache-cold timed step, from a per-dispatch kernel trace: each gdn
+    kernel's duration and workgroups, and the span from the first launch's start to the
+    last one's end."""
     import csv
     import glob
     rows = []
@@ -183,9 +224,9 @@ def summarize_launches(kt_dir, cmd):
     long_steps = [st for st in steps if len(st) == n]
     step = long_steps[len(long_steps) // 2] if long_steps else []
     wg = lambda r: int(r.get("Grid_Size", r.get("Grid_Size_X", 0))) // max(1, int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 1))))
-    lines = ["# launches of one cache-cold step of the hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, "
-             "chunk 64) in the library's default composition",
+    lines = ["# launches of one cache-cold step: " + title,
              "# command: " + cmd,
+             "composition: %s" % composition,
              "# timed steps of %d launches in the trace: %d (the middle one shown)" % (n, len(long_steps)),
              "kernel  workgroups  dur_us"]
     for r in step:
@@ -207,11 +248,13 @@ MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ
 N_CU = 256
 
 
-def summarize_counters(pmc_dir, kt_dir, cmd, title):
+def summarize_counters(pmc_dir, kt_dir, cmd, title, label, composition, calls):
     """Per-kernel MFMA and occupancy counters from one rocprofv3 --pmc pass of this script,
     with kernel durations from the kernel-trace run: executed MFMA flops (512 per bf16
     MOP) per launch and their rate, MFMA busy share (busy cycles over the per-XCD active
-    cycles x CUs x 4 SIMDs), waves per launch and LDS bank conflicts per launch."""
+    cycles x CUs x 4 SIMDs), mean resident waves per CU (SQ_WAVE_CYCLES counts quad-cycles:
+    x 4 over the kernel's cycles x CUs), waves and LDS bank conflicts per launch; then the
+    same summed over every launch of one call."""
     import csv
     import glob
     import numpy as np
@@ -222,14 +265,11 @@ def summarize_counters(pmc_dir, kt_dir, cmd, title):
             out += list(csv.DictReader(open(f)))
         return out
 
-    def short(name):
-        m = re.search(r"(gdn_\w+)<", name) or re.search(r"(gdn_\w+)\(", name)
-        return m.group(1) if m else None
-
+    short = _short_kernel
     per = {}
     for r in rows(pmc_dir, "*counter_collection.csv"):
         k = short(r["Kernel_Name"])
-        if k:
+        if k and k != "copy_probe":
             per.setdefault(k, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
             per[k][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
     dur = {}
@@ -242,7 +282,14 @@ def summarize_counters(pmc_dir, kt_dir, cmd, title):
              "per-slice redundancy included: not algorithmic)",
              "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x %d CUs x 4 SIMDs); "
              "GRBM_GUI_ACTIVE reads the active cycles summed over the 8 XCDs" % N_CU,
-             "source_digest: %s" % source_digest("hybrid")]
+             "# waves_per_cu = SQ_WAVE_CYCLES x 4 / (GRBM_GUI_ACTIVE / 8 x %d CUs): mean resident waves "
+             "per CU over the launch, idle CUs included" % N_CU,
+             "composition: %s" % composition,
+             "source_digest: %s" % source_digest(label if label == "decode" else "hybrid")]
+    tot = {}
+    for k in per:
+        for n, v in per[k].items():
+            tot[n] = tot.get(n, 0.0) + sum(v.values())
     for k in sorted(per):
         c = {n: float(np.mean(list(v.values()))) for n, v in per[k].items()}
         mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
@@ -254,9 +301,19 @@ def summarize_counters(pmc_dir, kt_dir, cmd, title):
         if c.get("GRBM_GUI_ACTIVE"):
             lines.append("%s mfma_busy: %.4f" % (k, c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
                                                   / (c["GRBM_GUI_ACTIVE"] / 8 * N_CU * 4)))
+        if c.get("GRBM_GUI_ACTIVE") and "SQ_WAVE_CYCLES" in c:
+            lines.append("%s waves_per_cu: %.3f" % (k, c["SQ_WAVE_CYCLES"] * 4 / (c["GRBM_GUI_ACTIVE"] / 8 * N_CU)))
+        lines.append("%s launches: %d (%.3g per call)" % (k, len(per[k].get("SQ_WAVES", {})),
+                                                       len(per[k].get("SQ_WAVES", {})) / calls))
         for n in ("SQ_WAVES", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"):
             if n in c:
                 lines.append("%s %s: %.6g" % (k, n, c[n]))
+    if tot.get("GRBM_GUI_ACTIVE"):
+        lines.append("per_call executed_flops: %.6g" % (tot.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / calls))
+        lines.append("per_call mfma_busy: %.4f" % (tot.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+                                                   / (tot["GRBM_GUI_ACTIVE"] / 8 * N_CU * 4)))
+        lines.append("per_call waves_per_cu: %.3f" % (tot.get("SQ_WAVE_CYCLES", 0.0) * 4
+                                                      / (tot["GRBM_GUI_ACTIVE"] / 8 * N_CU)))
     return "\n".join(lines) + "\n"
 
 
@@ -385,6 +442,10 @@ def bench_decode(args):
         step(i, evs[i])
     torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    if args.only_timed:
+        if args.copy_probe:
+            copy_probe(args.copy_probe, dev)
+        return
     wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, args.steps // 2))]
     for i, e in enumerate(wev):
         step(i, e)
@@ -408,7 +469,7 @@ def bench_decode(args):
                                "bf16 q/k/v/o, fp32 state, per-head gate" % B, "sequences": B},
         "roofline": {"bound": "hbm", "kernel": "gdn_decode", "achieved": gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": traffic_from_profiles("gdn_decode", source_digest("decode"), "decode"),
+                     "traffic": traffic_from_profiles("decode", "decode", source_digest("decode"), kernel="gdn_decode"),
                      "kernel_ms": ms_step, "algorithmic_bytes": nbytes},
         "timing": {"headline": "median cold-cache step (%d MiB scratch written before each step)"
                                % args.flush_mib if args.flush_mib else "median warm step",
@@ -441,6 +502,38 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+def workload_title(name):
+    spec = __import__("linear_attention_rnn_chunk_amd.inputs", fromlist=["CONFIGS"]).CONFIGS[name]
+    seqs = ("B=%d, T=%d" % (spec.n_seq, spec.seq_lens[0]) if len(set(spec.seq_lens)) == 1 and not spec.packed
+            else "%d packed sequences (%s tokens)" % (spec.n_seq, "+".join(map(str, spec.seq_lens))))
+    return "%s GDN layer (%s, %d/%d heads, d=%d, %s gate, chunk %d)" % (
+        name, seqs, spec.hk, spec.hv, spec.dk, "per-head" if spec.gate == "head" else "per-key-channel",
+        spec.chunk)
+
+
+def layer_problem(args, spec, compose, stages=0):
+    """The gdn_problem bench.py times for workload `spec` (fixed-length batch, or packed)."""
+    from linear_attention_rnn_chunk_amd import gdn
+    packed = spec.packed or len(set(spec.seq_lens)) > 1
+    chunk = args.chunk or spec.chunk
+    gate = gdn.GATE_KEY_CHANNEL if spec.gate == "channel" else gdn.GATE_HEAD
+    qdt = gdn.BF16 if spec.qkv_dtype == "bf16" else gdn.F32
+    odt = gdn.BF16 if args.arm == "bf16" else gdn.F32
+    arm = gdn.ARM_MFMA_BF16 if args.arm == "bf16" else gdn.ARM_FOLD_F32
+    return gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else spec.seq_lens[0], spec.hk, spec.hv,
+                            spec.dk, spec.dv, gate, chunk, qdt, odt, arm, compose, stages)
+
+
+COMPOSE_NAMES = ("auto", "split", "fused", "pipelined", "seqsplit")
+
+
+def resolved_composition(args):
+    """The composition gdn_chunk_fwd runs for this workload on the current device."""
+    from linear_attention_rnn_chunk_amd import gdn, inputs
+    spec = inputs.CONFIGS[args.config]
+    return COMPOSE_NAMES[gdn.plan_compose(layer_problem(args, spec, COMPOSE_NAMES.index(args.compose)))]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -449,21 +542,22 @@ def main():
     ap.add_argument("--config", default="hybrid")
     ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--chunk", type=int, default=0)
-    ap.add_argument("--compose", default="auto", choices=["auto", "split", "fused", "pipelined", "seqsplit"],
+    ap.add_argument("--compose", default="auto", choices=list(COMPOSE_NAMES),
                     help="auto: the library's choice (gdn_plan_compose says which); split: prep "
-                         "kernel then scan (timed per kernel); fused: tile waves inside the scan "
-                         "workgroup, one kernel; pipelined: scan segments with the next segment's "
-                         "prep beside each; seqsplit: parts of each sequence scanned side by side")
+                         "kernel then scan; fused: tile waves inside the scan workgroup, one "
+                         "kernel; pipelined: scan segments with the next segment's prep beside "
+                         "each; seqsplit: parts of each sequence scanned side by side")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="before each timed step, write this much scratch memory (larger than "
                          "the 256 MiB MALL and the L2s) so every step starts cache-cold; 0 = warm")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/ summaries from rocprofv3 output of this script and exit")
+                    help="write profiles/ summaries (kernel trace, HBM traffic) from rocprofv3 output "
+                         "of this script's --only-timed form and exit")
     ap.add_argument("--summarize-launches", metavar="KT_DIR",
-                    help="write profiles/ the launch sequence of one layer step from a rocprofv3 "
-                         "kernel trace of this script (default composition) and exit")
+                    help="write profiles/ the launch sequence of one timed step from a rocprofv3 "
+                         "kernel trace of this script and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write the MFMA / occupancy counter summary to profiles/ and exit")
     ap.add_argument("--peaks", action="store_true",
@@ -471,50 +565,51 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="time the one-token recurrent step instead: B sequences of the hybrid "
                          "layer's heads, each continuing from its own state; prints its own line")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run only the warm-up and the timed calls (no per-stage pass, no warm-cache "
+                         "pass): the form the profiling runs take, so every launch they see belongs "
+                         "to one of warmup + steps whole-layer calls")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of MIB MiB three times "
                          "(reads and writes MIB MiB each): the reference for scaling HBM counters")
     args = ap.parse_args()
 
-    if args.summarize_counters:
-        cmd = ("cd /tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " -d <out>/prof_mfma -o m -f csv -- "
-               "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --compose split")
-        txt = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cmd,
-                                 "hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)")
-        with open(os.path.join(ROOT, "profiles", "mfma_counters_hybrid.txt"), "w") as f:
-            f.write(txt)
-        print(txt)
-        return
-
-    if args.summarize_launches:
-        txt = summarize_launches(args.summarize_launches,
-                                 "cd /tmp && rocprofv3 --kernel-trace -d <out>/prof_lt -o lt -f csv -- "
-                                 "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu")
-        with open(os.path.join(ROOT, "profiles", "launches_hybrid_default.txt"), "w") as f:
-            f.write(txt)
-        print(txt)
-        return
-
-    if args.summarize_profiles:
-        label = "decode" if args.decode else "hybrid"
-        extra = " --decode %d" % args.decode if args.decode else ""
-        title = ("one-token step, %d sequences of the hybrid layer (16/48 heads, d=128)" % args.decode
-                 if args.decode else "hybrid GDN layer (B=1, T=32768, 16/48 heads, d=128, chunk 64)")
-        # the layer's kernels one launch each (split composition): the roofline's kernel
-        extra = extra or " --compose split"
-        cmds = ["cd /tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_kt -o kt -f csv -- "
-                "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu" + extra,
-                "cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/prof_fetch -o f -f csv -- "
-                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB + extra,
-                "cd /tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/prof_write -o w -f csv -- "
-                "python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu --copy-probe %d" % PROBE_MIB + extra]
-        trace_txt, traffic_txt = summarize_profiles(*args.summarize_profiles, cmds, label, title)
+    if args.summarize_counters or args.summarize_launches or args.summarize_profiles:
+        # run on the box that took the profiles: the library's choice of composition there
+        label = "decode" if args.decode else args.config
+        composition = "decode" if args.decode else resolved_composition(args)
+        calls = args.warmup + args.steps
+        run = ("python3 <repo>/bench.py --config %s --steps %d --warmup %d --no-cpu --only-timed%s%s"
+               % (args.config, args.steps, args.warmup,
+                  " --compose %s" % args.compose if args.compose != "auto" else "",
+                  " --decode %d" % args.decode if args.decode else ""))
+        title = (("one-token step, %d sequences of the hybrid layer (16/48 heads, d=128)" % args.decode)
+                 if args.decode else workload_title(args.config))
         os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-        with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.txt" % label), "w") as f:
-            f.write(trace_txt)
-        with open(os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % label), "w") as f:
-            f.write(traffic_txt)
-        print(trace_txt + traffic_txt)
+        out = []
+        if args.summarize_counters:
+            cmd = "cd /tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " -d <out>/prof_mfma -o m -f csv -- " + run
+            txt = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cmd, title,
+                                     label, composition, calls)
+            out.append(("mfma_counters_%s.txt" % label, txt))
+        if args.summarize_launches:
+            txt = summarize_launches(args.summarize_launches,
+                                     "cd /tmp && rocprofv3 --kernel-trace -d <out>/prof_lt -o lt -f csv -- " + run,
+                                     title, composition)
+            out.append(("launches_%s.txt" % label, txt))
+        if args.summarize_profiles:
+            cmds = ["cd /tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_kt -o kt -f csv -- " + run,
+                    "cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/prof_fetch -o f -f csv -- " + run
+                    + " --copy-probe %d" % PROBE_MIB,
+                    "cd /tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/prof_write -o w -f csv -- " + run
+                    + " --copy-probe %d" % PROBE_MIB]
+            trace_txt, traffic_txt = summarize_profiles(*args.summarize_profiles, cmds, label, composition,
+                                                        calls, title)
+            out += [("kernel_trace_%s.txt" % label, trace_txt), ("hbm_traffic_%s.txt" % label, traffic_txt)]
+        for name, txt in out:
+            with open(os.path.join(ROOT, "profiles", name), "w") as f:
+                f.write(txt)
+            print(txt)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -559,21 +654,13 @@ def main():
     q, k, v, g, beta = (shp(t(getattr(inp, n))) for n in ("q", "k", "v", "g", "beta"))
     h0 = t(inp.h0)
     gate = gdn.GATE_KEY_CHANNEL if spec.gate == "channel" else gdn.GATE_HEAD
-    qdt = gdn.BF16 if spec.qkv_dtype == "bf16" else gdn.F32
     odt_t = torch.bfloat16 if args.arm == "bf16" else torch.float32
-    arm = gdn.ARM_MFMA_BF16 if args.arm == "bf16" else gdn.ARM_FOLD_F32
-    req = {"auto": gdn.COMPOSE_AUTO, "split": gdn.COMPOSE_SPLIT, "fused": gdn.COMPOSE_FUSED,
-           "pipelined": gdn.COMPOSE_PIPELINED, "seqsplit": gdn.COMPOSE_SEQSPLIT}[args.compose]
-    mk = lambda compose, stages: gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else Tn, spec.hk,
-                                                  spec.hv, spec.dk, spec.dv, gate, chunk, qdt,
-                                                  gdn.BF16 if odt_t == torch.bfloat16 else gdn.F32, arm,
-                                                  compose, stages)
-    p_all = mk(req, gdn.STAGE_ALL)
-    composition = {gdn.COMPOSE_SPLIT: "split", gdn.COMPOSE_FUSED: "fused",
-                   gdn.COMPOSE_PIPELINED: "pipelined", gdn.COMPOSE_SEQSPLIT: "seqsplit"}[gdn.plan_compose(p_all)]
-    fused, whole = composition == "fused", composition != "split"
-    # the split composition's two stages, called one by one: the per-kernel timing
-    p_prep, p_scan = mk(gdn.COMPOSE_SPLIT, gdn.STAGE_PREP), mk(gdn.COMPOSE_SPLIT, gdn.STAGE_SCAN)
+    p_all = layer_problem(args, spec, COMPOSE_NAMES.index(args.compose))
+    composition = COMPOSE_NAMES[gdn.plan_compose(p_all)]
+    fused = composition == "fused"
+    # the split composition's two stages, called one by one: the per-stage view
+    p_prep = layer_problem(args, spec, gdn.COMPOSE_SPLIT, gdn.STAGE_PREP)
+    p_scan = layer_problem(args, spec, gdn.COMPOSE_SPLIT, gdn.STAGE_SCAN)
     o = torch.empty((B, Tn, spec.hv, spec.dv), dtype=odt_t, device=dev)
     hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -581,27 +668,27 @@ def main():
                      device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None, per_kernel=False):
-        if whole and not per_kernel:  # one call (fused: one kernel; pipelined: its segments)
-            if ev is not None:
-                ev[0].record(stream)
-                ev[1].record(stream)
-            rc = gdn.chunk_fwd_raw(p_all, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
-            if ev is not None:
-                ev[2].record(stream)
-            if rc:
-                raise gdn.GdnError(rc, "gdn_chunk_fwd")
-            return
-        if ev is not None:
-            ev[0].record(stream)
-        rc = gdn.chunk_fwd_raw(p_prep, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
-        if ev is not None:
-            ev[1].record(stream)
-        rc |= gdn.chunk_fwd_raw(p_scan, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
-        if ev is not None:
-            ev[2].record(stream)
+    def call(prob):
+        rc = gdn.chunk_fwd_raw(prob, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
         if rc:
             raise gdn.GdnError(rc, "gdn_chunk_fwd")
+
+    def step(ev=None):  # one whole gdn_chunk_fwd, events on the library's stream around it
+        if ev is not None:
+            ev[0].record(stream)
+        call(p_all)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def stages(ev=None):  # the split composition's prep then scan, an event between them
+        if ev is not None:
+            ev[0].record(stream)
+        call(p_prep)
+        if ev is not None:
+            ev[1].record(stream)
+        call(p_scan)
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -609,11 +696,11 @@ def main():
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
 
-    # Timed region: exactly `steps` layer steps between two device synchronisations.  Each
-    # step is preceded (outside its events) by a scratch write that evicts the caches, so
+    # Timed region: exactly `steps` layer calls between two device synchronisations.  Each
+    # call is preceded (outside its events) by a scratch write that evicts the caches, so
     # the step time is cache-cold; the headline is the median step.
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -622,46 +709,56 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
-    prep_v = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    scan_v = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     ms_step = float(np.median(step_ms))
-    prep_ms, scan_ms = float(np.median(prep_v)), float(np.median(scan_v))
-    if composition in ("pipelined", "seqsplit"):
-        # per-kernel times (the roofline's dominant kernel): the split composition's two
-        # stages, timed the same way in a second pass of as many cache-cold steps
-        step(per_kernel=True)  # untimed: first use of the split kernels' launch attributes
-        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            if flush is not None:
-                flush.fill_(i & 0xFF)
-            step(kev[i], per_kernel=True)
+    prep_ms = scan_ms = warm_ms = None
+    if not args.only_timed:
+        if not fused:
+            # the split composition's stages, timed the same way in a second pass of as many
+            # cache-cold steps (one untimed call first: launch attributes of its kernels)
+            stages()
+            kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                if flush is not None:
+                    flush.fill_(i & 0xFF)
+                stages(kev[i])
+            torch.cuda.synchronize()
+            prep_ms = float(np.median([e[0].elapsed_time(e[1]) for e in kev]))
+            scan_ms = float(np.median([e[1].elapsed_time(e[2]) for e in kev]))
+        # warm-cache median for context (same work, no eviction in between)
+        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, args.steps // 2))]
+        for e in wev:
+            step(e)
         torch.cuda.synchronize()
-        prep_ms = float(np.median([e[0].elapsed_time(e[1]) for e in kev]))
-        scan_ms = float(np.median([e[1].elapsed_time(e[2]) for e in kev]))
-    # warm-cache median for context (same work, no eviction in between)
-    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, args.steps // 2))]
-    for e in wev:
-        step(e)
-    torch.cuda.synchronize()
-    warm_ms = float(np.median([e[0].elapsed_time(e[2]) for e in wev]))
+        warm_ms = float(np.median([e[0].elapsed_time(e[1]) for e in wev]))
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
-    log("%s: ms/step %.4f median cold (min %.4f; %sprep %.4f, scan %.4f), warm %.4f, wall %.3f s for %d steps"
-        % (composition, ms_step, step_ms.min(), "split kernels: " if composition in ("pipelined", "seqsplit") else "",
-           prep_ms, scan_ms, warm_ms, wall, args.steps))
+    log("%s: ms/step %.4f median cold (min %.4f), wall %.3f s for %d steps; split stages: prep %s, scan %s; warm %s"
+        % (composition, ms_step, step_ms.min(), wall, args.steps, prep_ms, scan_ms, warm_ms))
+    if args.only_timed:
+        if args.copy_probe:
+            copy_probe(args.copy_probe, dev)
+        return
 
     alg = algorithmic(spec, chunk)
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if args.arm == "bf16" else MFMA_F32_PEAK_TFLOPS
-    dom = "scan" if scan_ms >= prep_ms else "prep"
-    dom_ms = scan_ms if dom == "scan" else prep_ms
-    # the fused kernel moves only the layer's compulsory bytes (no tiles through HBM)
-    dom_bytes = alg["layer_bytes"] if fused else alg[dom + "_bytes"]
-    achieved_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kernel_name = "gdn_scan" if dom == "scan" else "gdn_prep"
+    flops = scope_flops(spec, chunk)
+    layer_bytes = alg["layer_bytes"]
+    # The roofline's kernel is the timed call itself: every launch of one gdn_chunk_fwd (a
+    # pipelined call is one prep launch and one scan launch per segment, each carrying the
+    # next segment's prep), bracketed by HIP events on the library's stream.  Its
+    # algorithmic bytes are the layer's compulsory bytes; what the composition moves on top
+    # (the tiles' round trip through HBM) is reported beside them, not counted as work.
+    achieved_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
     digest = source_digest("hybrid")
-    traffic = traffic_from_profiles(kernel_name, digest, "hybrid")
+    traffic = traffic_from_profiles(args.config, composition, digest)
     tokens_s = spec.tokens / (ms_step * 1e-3)
+    kernels = {"split": "gdn_prep_head + gdn_scan", "pipelined": "gdn_prep_head + gdn_scan per segment",
+               "fused": "gdn_scan (fused)", "seqsplit": "gdn_prep_head + 2 x gdn_scan + gdn_seq_chain"}
+    if gate == gdn.GATE_KEY_CHANNEL:
+        kernels["split"] = "gdn_prep_chan + gdn_scan"
+    if packed:
+        kernels["split"] = "gdn_chunk_table + " + kernels["split"]
 
     rec = {
         "metric": METRIC,
@@ -676,31 +773,39 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if args.arm == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": "%s GDN layer prefill: B=%d, T=%d, %d key / %d value heads, "
+        "config": {"workload": "%s GDN layer prefill: %s, %d key / %d value heads, "
                                "dk=dv=%d, %s gate, chunk %d%s"
-                               % (spec.name, spec.n_seq, spec.tokens // spec.n_seq, spec.hk, spec.hv,
-                                  spec.dk, "per-head" if gate == gdn.GATE_HEAD else "per-key-channel",
+                               % (spec.name, ("B=%d, T=%d" % (spec.n_seq, spec.tokens // spec.n_seq)) if not packed
+                                  else "%d packed sequences (%s tokens)" % (spec.n_seq, "+".join(map(str, spec.seq_lens))),
+                                  spec.hk, spec.hv, spec.dk,
+                                  "per-head" if gate == gdn.GATE_HEAD else "per-key-channel",
                                   chunk, ", h0" if spec.h0 else ""),
                    "tokens": spec.tokens, "arm": args.arm, "composition": composition},
-        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel_ms": dom_ms, "algorithmic_bytes": dom_bytes,
-                     "composition": "fused" if fused else "split"},
-        "mfma": {"definition": "algorithmic flops / kernel time / dense peak",
-                 "peak_tflops": peak_mfma,
-                 "prep_frac": (alg["prep_flops"] / (prep_ms * 1e-3) / (peak_mfma * 1e12)) if not fused else None,
-                 "scan_frac": (alg["scan_flops"] + (alg["prep_flops"] if fused else 0)) / (scan_ms * 1e-3)
-                 / (peak_mfma * 1e12),
-                 "layer_frac": (alg["prep_flops"] + alg["scan_flops"]) / (ms_step * 1e-3)
-                 / (peak_mfma * 1e12)},
-        "kernels_ms": ({"prep": prep_ms, "scan": scan_ms} if not fused else {"scan_fused": scan_ms}),
-        "kernels_composition": "fused" if fused else "split",
+        "roofline": {"bound": "hbm", "kernel": "gdn_chunk_fwd [%s: %s]" % (composition, kernels[composition]),
+                     "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic, "kernel_ms": ms_step,
+                     "algorithmic_bytes": layer_bytes,
+                     "composition_overhead_bytes": 0 if fused else composition_overhead_bytes(spec, chunk),
+                     "composition": composition},
+        "mfma": {"definition": "algorithmic flops of the scope table (K K^T, Q K^T per key head; solve, "
+                               "W/U' folds, state update and output per value head) / time / dense peak",
+                 "peak_tflops": peak_mfma, "flops": flops,
+                 "layer_frac": flops / (ms_step * 1e-3) / (peak_mfma * 1e12)},
         "timing": {"headline": "median cold-cache step (%d MiB scratch written before each step)"
                                % args.flush_mib if args.flush_mib else "median warm step",
                    "min_ms": float(step_ms.min()), "warm_median_ms": warm_ms},
-        "layer_hbm_frac": alg["layer_bytes"] / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "source_digest": digest,
     }
+    if prep_ms is not None:
+        # the split composition's two stages, each timed with its own events in a second
+        # pass of as many cache-cold steps (context: the per-stage view of the same work)
+        prep_flops = alg["prep_flops"]
+        rec["split_stages"] = {
+            "prep_ms": prep_ms, "scan_ms": scan_ms,
+            "prep_mfma_frac": prep_flops / (prep_ms * 1e-3) / (peak_mfma * 1e12),
+            "scan_mfma_frac": (flops - prep_flops) / (scan_ms * 1e-3) / (peak_mfma * 1e12),
+            "prep_flops": prep_flops, "scan_flops": flops - prep_flops,
+        }
     if args.copy_probe:
         rec["copy_probe_bytes"] = copy_probe(args.copy_probe, dev)
     if args.peaks:

@@ -114,22 +114,48 @@ typedef struct gdn_problem {
   int32_t stages;       /* GDN_STAGE_ALL, or PREP / SCAN alone (split composition) */
 } gdn_problem;
 
-/* Checks a problem description on the host (no device work).  Returns GDN_OK,
- * GDN_E_NULL, GDN_E_SHAPE or GDN_E_UNSUPPORTED. */
+/* gdn_validate -- checks a problem description on the host (no device work): every
+ * size, width, dtype, gate form, chunk and composition must lie in the supported domain,
+ * and anything else is refused with a typed code rather than computed (the logismos issue
+ * #46 page: unsupported inputs fail explicitly, section "Acceptance"; grouped-head
+ * mapping, initial/final state, chunk boundaries, input domains and precision kept
+ * explicit, section "Remaining work").
+ *   p  the problem; read only
+ * Returns GDN_OK, GDN_E_NULL (p is NULL), GDN_E_SHAPE (negative or inconsistent sizes,
+ * tokens with no sequence) or GDN_E_UNSUPPORTED (outside the domain). */
 gdn_status gdn_validate(const gdn_problem* p);
 
-/* Bytes of device workspace gdn_chunk_fwd needs for *p (written to *bytes).
- * Same return codes as gdn_validate. */
+/* gdn_workspace_bytes -- bytes of device workspace gdn_chunk_fwd needs for *p, written to
+ * *bytes.  The workspace holds the state-independent per-chunk tiles of the chunk form (T
+ * and P of every chunk: the stratat.com page, section "What this is", one unit-lower-
+ * triangular solve per chunk; the ROCm/rocm-libraries KDA chunkwise page, sections
+ * "Summary" and "Levers": tiles formed sequence-parallel, then a serial scan, with a tile
+ * round trip through HBM), plus the composition's own buffers (the state carried between
+ * pipelined segments; a pipelined request keeps only two segments of tiles).  Host-only.
+ *   p      the problem; read only
+ *   bytes  out: the size (0 when nothing is needed); NULL is refused
+ * Same return codes as gdn_validate, plus GDN_E_NULL for a NULL `bytes`. */
 gdn_status gdn_workspace_bytes(const gdn_problem* p, size_t* bytes);
 
-/* The composition gdn_chunk_fwd runs for *p on the current device (written to *compose:
- * GDN_COMPOSE_SPLIT, _FUSED or _PIPELINED): the requested one, or for GDN_COMPOSE_AUTO the
- * library's choice, which depends on the device's compute-unit count.  Host-only (a
- * device attribute query, no device work); same return codes as gdn_validate. */
+/* gdn_plan_compose -- the composition gdn_chunk_fwd runs for *p on the current device,
+ * written to *compose (GDN_COMPOSE_SPLIT, _FUSED, _PIPELINED or _SEQSPLIT): the requested
+ * one, or for GDN_COMPOSE_AUTO the library's measured choice, which depends on the
+ * device's compute-unit count (split versus fused is a measured choice on the
+ * ROCm/rocm-libraries KDA chunkwise page, sections "Levers" and "The interesting result
+ * is a negative one").  Host-only: a device attribute query, no device work.
+ *   p        the problem; read only
+ *   compose  out; NULL is refused with GDN_E_NULL
+ * Same return codes as gdn_validate. */
 gdn_status gdn_plan_compose(const gdn_problem* p, int32_t* compose);
 
 /*
- * gdn_chunk_fwd -- chunkwise gated delta-rule prefill.
+ * gdn_chunk_fwd -- chunkwise gated delta-rule prefill: the rule above for every sequence
+ * and value head, evaluated per chunk by a unit-lower-triangular solve and GEMM-shaped
+ * folds (the stratat.com page, section "What this is") and a serial scan of the state over
+ * the chunks (the ROCm/rocm-libraries KDA chunkwise page, section "Summary"), under the
+ * argument contract of the logismos issue #46 page (Sep 6 / Sep 8 activity: K-first
+ * state, precomputed beta and natural-log g, grouped heads, immutable h0, separate final
+ * state; "Verified implementation boundary": sticky numerical status).
  *   q, k        [total_tokens][hk][dk]   qkv_dtype, 16-byte aligned
  *   v           [total_tokens][hv][dv]   qkv_dtype, 16-byte aligned
  *   g           fp32 natural-log decay, [total_tokens][hv] or [total_tokens][hv][dk]
@@ -183,14 +209,20 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, c
                            const float* g, const float* beta, const float* h_in, void* o,
                            float* h_out, uint32_t* status, void* stream);
 
-/* Static text for a host return code. */
+/* gdn_error_string -- static text naming a host return code (the explicit refusals of the
+ * logismos issue #46 page, section "Acceptance"); "unknown error code" for any other
+ * value.  Never NULL; the caller does not free it. */
 const char* gdn_error_string(int32_t code);
 
-/* Text naming the device status bits set in `bits` ("ok" when none).  The
- * returned pointer refers to thread-local storage valid until the next call. */
+/* gdn_status_string -- text naming the device status bits set in `bits` ("ok" when none,
+ * "|"-separated names, "unknown(0x..)" for bits the library does not define): the sticky
+ * numerical status of the logismos issue #46 page ("Verified implementation boundary",
+ * nonfinite inputs and results classified before anything is published).  The returned
+ * pointer refers to thread-local storage, valid until this thread's next call. */
 const char* gdn_status_string(uint32_t bits);
 
-/* GDN_ABI_VERSION of the loaded library. */
+/* gdn_abi_version -- GDN_ABI_VERSION of the loaded library (library bookkeeping, no page
+ * defines it): a caller built against this header checks it before the first call. */
 int32_t gdn_abi_version(void);
 
 #ifdef __cplusplus

@@ -17,6 +17,8 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   if (p->n_seq < 0 || p->total_tokens < 0 || p->seq_len < 0 || p->hk < 1 || p->hv < 1)
     return GDN_E_SHAPE;
   if (p->seq_len > 0 && (int64_t)p->n_seq * p->seq_len != p->total_tokens) return GDN_E_SHAPE;
+  // tokens that belong to no sequence
+  if (p->n_seq == 0 && p->total_tokens > 0) return GDN_E_SHAPE;
   if (p->hv % p->hk != 0) return GDN_E_UNSUPPORTED;
   if (!(p->dk == 32 || p->dk == 64 || p->dk == 128)) return GDN_E_UNSUPPORTED;
   if (!(p->dv == 32 || p->dv == 64 || p->dv == 128)) return GDN_E_UNSUPPORTED;
@@ -85,12 +87,20 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   if (pl.max_slots * pl.hv > INT32_MAX) return GDN_E_UNSUPPORTED;
   if ((int64_t)pl.n_seq * pl.hv * (pl.dv / 32) > INT32_MAX) return GDN_E_UNSUPPORTED;
 
+  // Pipelined composition on sequences longer than two segments: only the tiles of the
+  // segment being scanned and of the next one are live, so the tile buffers can be a ring
+  // of two segments per sequence.  An explicit PIPELINED request sizes the workspace for
+  // the ring; AUTO may still pick split, so it sizes for every chunk (the ring fits in it).
+  const int32_t seg = kSegTokens / pl.chunk;
+  pl.tile_ring = (pl.pipe_ok && !pl.varlen && pl.chunks_per_seq > 2 * seg) ? seg : 0;
+  pl.tile_slots = (pl.tile_ring && p->compose == GDN_COMPOSE_PIPELINED) ? (int64_t)pl.n_seq * 2 * seg
+                                                                        : pl.max_slots;
   const size_t esz = pl.arm_f32 ? 4 : 2;
   size_t off = 0;
   pl.off_table = off;
   off = round_up(off + (pl.varlen ? 2 * sizeof(int32_t) * (size_t)(pl.n_seq + 1) : 0), 256);
   // split composition: T and P of every chunk pass through the workspace
-  const size_t tile = pl.fused ? 0 : (size_t)pl.max_slots * pl.hv * gdn::tile_elems(C) * esz;
+  const size_t tile = pl.fused ? 0 : (size_t)pl.tile_slots * pl.hv * gdn::tile_elems(C) * esz;
   pl.off_T = off;
   off = round_up(off + tile, 256);
   pl.off_P = off;
@@ -106,7 +116,7 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   // per-head gate with fp32 inputs or the fp32 arm: K and Q in the arm's element type,
   // written by the sequence-parallel stage so the scan copies them without converting
   pl.kq_ws = !pl.gate_channel && (pl.qkv_f32 || pl.arm_f32);
-  const size_t kq = pl.kq_ws ? (size_t)pl.max_slots * pl.hk * C * pl.dk * esz : 0;
+  const size_t kq = pl.kq_ws ? (size_t)pl.tile_slots * pl.hk * C * pl.dk * esz : 0;
   pl.off_K = off;
   off = round_up(off + kq, 256);
   pl.off_Q = off;

@@ -308,6 +308,14 @@ __device__ __forceinline__ bool prep_slot(const Params& p, int64_t m, int64_t& s
   return true;
 }
 
+// Where the tiles of logical chunk slot `slot` (fixed-length: n * chunks_per_seq + c) are
+// stored: the slot itself, or in the pipelined ring slot n * 2 R + c mod 2 R.
+__device__ __forceinline__ int64_t store_slot(const Params& p, int64_t slot) {
+  if (!p.tile_ring) return slot;
+  const int64_t n = slot / p.chunks_per_seq, c = slot - n * p.chunks_per_seq;
+  return n * (2 * p.tile_ring) + c % (2 * p.tile_ring);
+}
+
 // ---------------------------------------------------- chunk table --------
 // Sanitised bounds b_0 = 0, b_i = min(total, max(0, max_{1<=j<=i} cu_j)), b_n = total,
 // so every index stays inside [0, total] whatever cu_seqlens holds; any difference
@@ -765,7 +773,7 @@ __device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, 
   constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32;
   const int i = lane & 15, g = lane >> 4;
   const int kh = U.kh, j = U.j, L = U.L, h = kh * (p.hv / p.hk) + j;
-  const int64_t slot = U.slot;
+  const int64_t slot = store_slot(p, U.slot);
   float* Gs = S + NTRI * kTile;
   float* Bs = Gs + C;
   uint32_t bad = tile_sweep<C>(U.R.xl, U.R.bl, L, lane, Gs, Bs);
@@ -869,6 +877,7 @@ __device__ __forceinline__ void prep_role(const Params& p) {
     int64_t slot, t0;
     int n, L;
     if (!prep_slot(p, 8 * k + x, slot) || !locate_chunk(p, C, slot, n, t0, L)) continue;
+    slot = store_slot(p, slot);  // (from here on: where the tiles go)
     const int h0 = kh * group, rg = lane < L ? lane : L - 1;
     TileRegs<DK, C, QF32> R;
     tile_loads<DK, C, QF32>(p, t0, L, kh, h0, lane, R);
@@ -1345,9 +1354,11 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     const int64_t b = (int64_t)nr * p.seq_len;
     s0 = b + min64(p.seq_len, (int64_t)cb * C);
     s1 = b + min64(p.seq_len, (int64_t)ce * C);
-    slot0 = (int64_t)nr * p.chunks_per_seq + cb;
+    slot0 = store_slot(p, (int64_t)nr * p.chunks_per_seq + cb);  // a ring launch stays in one segment
   }
-  const bool vzero = PARTS && kind == 1, no_out = PARTS && kind == 1;
+  // kind 1 (a transition) has no outputs; kind 0 of a part after the first scans from a
+  // zero state, so its outputs are not final either (the rescan writes them)
+  const bool vzero = PARTS && kind == 1, no_out = PARTS && (kind == 1 || (kind == 0 && part > 0));
   const int nch = (int)((s1 - s0 + C - 1) / C);
   uint32_t bad = 0;
 
@@ -1611,7 +1622,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) nf |= (__float_as_uint(o[u][nt][j]) & 0x7F800000u) + 0x00800000u;
-      bad |= flag_if(!no_out && (nf & 0x80000000u), GDN_ST_NONFINITE_OUTPUT);
+      bad |= flag_if(nf & 0x80000000u, GDN_ST_NONFINITE_OUTPUT);
       // rows of this chunk: uniform base plus the lane's fixed row offsets
       char* ob = (char*)p.o + ((t0 * hvs + h) * (int64_t)DV + 32 * slice) * OSZ;
       // lane (i, g) of tile nt holds row 16 nt + i, slice columns 8 g .. 8 g + 7 (the
@@ -1627,8 +1638,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           *(u32x4*)a = (u32x4){w0.x, w0.y, w1.x, w1.y};
         }
       };
-      if (no_out) {
-      } else if (L == C) {
+      if (L == C) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st(nt);
       } else {
@@ -1637,6 +1647,10 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           if (16 * nt + i < L) st(nt);
       }
     };
+    if (no_out) {  // a part whose outputs are not final: only the barriers
+      for (int ci = 0; ci <= nch; ++ci) __syncthreads();
+      return;
+    }
     if (nch > 0) load_q(0, 0);
     wait_vm<0>();
     __syncthreads();
@@ -1998,12 +2012,9 @@ bool set_lds_once(Fn fn, size_t lds) {
   return true;
 }
 
-// Pipelined composition: the scan in chunk-aligned segments (the state carried in
-// `carry`), each launch also running the next segment's prep in workgroups after the
-// scan's own.  Segments are kSegTokens tokens long (the last one may be shorter): on the
-// hybrid layer (32,768 tokens, chunk 64) 16 segments of 32 chunks measured 0.748 ms,
-// against 0.844 with 8, 0.790 with 12, 0.826 with 32 and 0.922 for the split composition.
-constexpr int kSegTokens = 2048;
+// Pipelined composition: the scan in chunk-aligned segments of kSegTokens tokens (the
+// state carried in `carry`), each launch also running the next segment's prep in
+// workgroups after the scan's own.
 
 template <class Arm, int DK, int C, bool QF32>
 gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int nprep, hipStream_t st) {
@@ -2016,6 +2027,7 @@ gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int np
   using SL = ScanLds<Arm, DK, C, false, QF32, false>;
   if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false>, SL::BYTES)) return GDN_E_LAUNCH;
   Params q = prm;
+  q.tile_ring = pl.tile_ring;  // (the plan's ring half is one segment, SEG chunks)
   q.prep_cb = 0;
   q.prep_ce = cut(1);
   const int64_t m0 = (int64_t)pl.n_seq * q.prep_ce;  // 0 when the first segment is empty

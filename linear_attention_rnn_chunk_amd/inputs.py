@@ -22,7 +22,8 @@ packed    4 sequences 65536/32768/24576/8192 (131072 tokens), 16/48 heads,
           d=128, bf16, chunk 64, per-sequence h0
 ========  ===================================================================
 
-Draw order per seed (numpy PCG64): q, k, v, beta logits, gate, h0.
+Draw order per seed (numpy PCG64): q, k, v, beta logits, gate, h0.  With
+``qk_same`` q is then replaced by a copy of k (same values, same bf16 bits).
 q and k are N(0,1), L2-normalised per (token, head) in fp32; q is then scaled
 by dk^-1/2 except in ``tiny``; v ~ N(0,1); beta = sigmoid(N(0,1)); the gate is
 a natural-log decay (``clip5``: -softplus(N) clipped to [-5, 0]; ``half``:
@@ -55,6 +56,7 @@ class Spec:
     o_dtype: str = "bf16"
     seed: int = 0
     beta_law: str = "sigmoid"      # sigmoid | one | zero | eps
+    qk_same: bool = False          # q is a copy of k (after k's normalisation and cast)
 
     @property
     def tokens(self) -> int:
@@ -182,6 +184,8 @@ def make(spec, seed: Optional[int] = None) -> Inputs:
             raise ValueError(law)
 
     h0 = (np.float32(0.1) * _normal(rng, (spec.n_seq, hv, dk, dv))) if spec.h0 else None
+    if spec.qk_same:  # (q's own draw above keeps the draw order of the other streams)
+        q = k.copy()
 
     if spec.qkv_dtype == "bf16":
         q, k, v = bf16_round_bits(q), bf16_round_bits(k), bf16_round_bits(v)

@@ -58,8 +58,12 @@ def oracle_ref(inp, units=None, want_o=True, mutant=oracle.CORRECT):
 
 
 def rel(x, ref):
+    """NaN-aware relative L2 of a GPU result x against the fp64 oracle's ref.  ref is first
+    taken to fp32 (the exponent range of every output, fp32 or bf16): a value below that
+    range (a state decayed by e^-160, say) has no representation but zero there, so it
+    cannot count as error."""
     x = np.asarray(x, np.float64)
-    ref = np.asarray(ref, np.float64)
+    ref = np.asarray(ref, np.float64).astype(np.float32).astype(np.float64)
     if not np.all(np.isfinite(x)):
         return float("inf")
     den = np.linalg.norm(ref.ravel())

@@ -40,6 +40,25 @@ def test_flop_counts_per_chunk():
     assert alg["scan_flops"] == nch * hv * (6 * C * dk * dv + 2 * C * C * dv)
 
 
+def test_scope_table_flops_and_bytes_of_every_workload():
+    # the hot-path scope table's per-workload figures, counted per term:
+    #   per (chunk, key head) 2 C^2 dk; per (chunk, value head) C^3/3 + C^2 (dk + dv)
+    #   + 4 C dk dv + 2 C dk dv + C^2 dv
+    f = bench.scope_flops(inputs.CONFIGS["hybrid"], 64)
+    terms = [8192 * 2 * 64 * 64 * 128, 24576 * 64 ** 3 / 3, 24576 * 64 * 64 * 256,
+             24576 * 4 * 64 * 128 * 128, 24576 * (2 * 64 * 128 * 128 + 64 * 64 * 128)]
+    assert abs(f - sum(terms)) < 1 and abs(f / 1e9 - 204.01) < 0.01
+    assert abs(bench.scope_flops(inputs.CONFIGS["kda"], 32) / 1e9 - 124.91) < 0.01
+    assert abs(bench.scope_flops(inputs.CONFIGS["packed"], 64) / 1e9 - 816.04) < 0.01
+    assert abs(bench.scope_flops(inputs.CONFIGS["single"], 64) / 1e9 - 9.216) < 0.001
+    # compulsory bytes: the per-channel gate [T][hv][dk] fp32 is 512 MiB of the kda layer
+    assert bench.algorithmic(inputs.CONFIGS["kda"], 32)["layer_bytes"] == 1_619_001_344
+    assert bench.algorithmic(inputs.CONFIGS["packed"], 64)["layer_bytes"] == 4_370_464_768
+    assert bench.algorithmic(inputs.CONFIGS["single"], 64)["layer_bytes"] == 68_681_728
+    # the tile round trip of the split-type compositions (T and P written and read back)
+    assert bench.composition_overhead_bytes(inputs.CONFIGS["hybrid"], 64) == 2 * 512 * 48 * 2 * 6 * 1024
+
+
 def test_decode_bytes():
     # 256 sequences x 48 value heads: fp32 state in and out, v and o bf16, g and beta;
     # q and k per key head
@@ -82,7 +101,7 @@ def test_launch_summary_picks_a_timed_step(tmp_path):
         w = csv.DictWriter(f, fieldnames=fields)
         w.writeheader()
         w.writerows(rows)
-    txt = bench.summarize_launches(str(d), "cmd")
+    txt = bench.summarize_launches(str(d), "cmd", "hybrid", "pipelined")
     assert "timed steps of 5 launches in the trace: 5" in txt
     lines = [l for l in txt.splitlines() if l.startswith("gdn_")]
     assert lines == ["gdn_prep_head  512  20.0", "gdn_scan  256  48.0", "gdn_scan  256  48.0",

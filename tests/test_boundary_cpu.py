@@ -56,6 +56,8 @@ def P(**kw):
     (dict(total_tokens=-5), gdn.GDN_E_SHAPE),
     (dict(hk=0), gdn.GDN_E_SHAPE),
     (dict(total_tokens=255), gdn.GDN_E_SHAPE),           # != n_seq * seq_len
+    (dict(n_seq=0, seq_len=0), gdn.GDN_E_SHAPE),          # tokens that belong to no sequence
+    (dict(n_seq=0, total_tokens=0, seq_len=0), gdn.GDN_OK),
     (dict(hv=5), gdn.GDN_E_UNSUPPORTED),                 # hv % hk
     (dict(dk=96), gdn.GDN_E_UNSUPPORTED),
     (dict(dv=256), gdn.GDN_E_UNSUPPORTED),
@@ -145,6 +147,23 @@ def test_workspace_bytes_scales_with_tiles():
     # packed form: slots bounded by ceil(total / C) + n_seq, plus the chunk table
     pk = gdn.workspace_bytes(P(n_seq=3, seq_len=0, chunk=64))
     assert pk >= 2 * (4 + 3) * hv * 3072 * 2
+
+
+def test_pipelined_request_keeps_two_segments_of_tiles():
+    # sequences of 512 chunks (64 tokens each): a pipelined call keeps the tiles of the
+    # segment it scans and of the next one (2 x 32 chunks per sequence), split keeps all
+    r256 = lambda x: (x + 255) // 256 * 256
+    kw = dict(n_seq=2, total_tokens=2 * 32768, seq_len=32768, hk=16, hv=48)
+    tile = 6 * 512 * 2                                # T or P of one chunk and value head, bf16
+    carry = 2 * 48 * 128 * 128 * 4                    # the state between segments
+    assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_PIPELINED, **kw)) == 2 * r256(2 * 64 * 48 * tile) + carry
+    assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_SPLIT, **kw)) == 2 * r256(2 * 512 * 48 * tile)
+    # AUTO may still pick split on a device with no idle units: it sizes for every chunk
+    assert gdn.workspace_bytes(P(**kw)) == 2 * r256(2 * 512 * 48 * tile) + carry
+    # two segments or fewer: no ring, every chunk its own slot
+    short = dict(n_seq=1, total_tokens=4096, seq_len=4096, hk=16, hv=16)
+    assert gdn.workspace_bytes(P(compose=gdn.COMPOSE_PIPELINED, **short)) == \
+        gdn.workspace_bytes(P(compose=gdn.COMPOSE_SPLIT, **short)) + 16 * 128 * 128 * 4
 
 
 # fake, well-aligned device addresses: the host checks below return before any launch

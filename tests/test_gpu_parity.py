@@ -45,6 +45,44 @@ def test_length_and_gate_sweep(T, mode, arm):
     _check(inputs.make(spec), arm, label="T=%d %s" % (T, mode))
 
 
+# beta at its edges: 0 (no write: pure decay of h0, T = I), 1 (full erase: the largest
+# off-diagonal A, the hardest solve) and 1e-6 (the write at first order: decayed linear
+# attention scaled by 1e-6; no h0, so the outputs are that small term alone)
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+@pytest.mark.parametrize("gate,law", [("head", "half"), ("channel", "uniform5"), ("channel", "uniform05")])
+@pytest.mark.parametrize("beta_law", ["zero", "one", "eps"])
+@pytest.mark.parametrize("T", [1, 65, 4099])
+def test_beta_edge_sweep(T, beta_law, gate, law, arm):
+    spec = inputs.Spec("beta", (T,), 2, 4, 64, 64, qkv_dtype="bf16", gate=gate, gate_law=law,
+                       h0=beta_law != "eps", chunk=32 if gate == "channel" else 64, beta_law=beta_law,
+                       seed=700 + T)
+    _check(inputs.make(spec), arm, label="T=%d beta=%s %s/%s" % (T, beta_law, gate, law))
+
+
+# The delta rule stores v exactly: with beta = 1, unit keys and q = k, o_t = v_t for every
+# token whatever the gate and h0 (the state's read along k_t after the write is v_t).  On
+# fp32 inputs (|k| = 1 to fp32 rounding) the GPU's o is checked against v itself, at the
+# arm's bound: the identity is exact, so any excess is the kernel's own error.
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+@pytest.mark.parametrize("gate,law", [("head", "half"), ("head", "clip5"), ("channel", "uniform5"),
+                                      ("channel", "uniform05")])
+@pytest.mark.parametrize("T", [1, 65, 4099])
+def test_unit_key_equal_query_returns_value(T, gate, law, arm):
+    spec = inputs.Spec("o=v", (T,), 2, 4, 64, 64, qkv_dtype="f32", gate=gate, gate_law=law, h0=True,
+                       chunk=32 if gate == "channel" else 64, beta_law="one", qk_same=True,
+                       q_scale=False, o_dtype="f32", seed=800 + T)
+    inp = inputs.make(spec)
+    assert np.array_equal(inp.q, inp.k) and np.all(inp.beta == 1.0)
+    o, hT, _ = run_gpu(inp, arm=arm, o_dtype=torch.float32)
+    ev = rel(to_np64(o), inp.v.astype(np.float64))
+    o_ref, h_ref = oracle_ref(inp)
+    assert rel(o_ref, inp.v.astype(np.float64)) < 1e-6   # the identity, on these inputs
+    eo, eh = rel(to_np64(o), o_ref), rel(to_np64(hT), h_ref)
+    print("o=v T=%d %s/%s arm=%s: rel-L2 o-v %.3e, vs oracle o %.3e hT %.3e" % (T, gate, law, arm, ev, eo, eh),
+          flush=True)
+    assert ev <= BOUND[arm] and eo <= BOUND[arm] and eh <= BOUND[arm], (ev, eo, eh)
+
+
 @pytest.mark.parametrize("arm", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(32, 32), (32, 128), (64, 64), (128, 32), (128, 64), (128, 128)])
 @pytest.mark.parametrize("chunk", [32, 64])

@@ -252,6 +252,34 @@ def test_P9_packed_sequences_equal_independent_runs():
     assert rel_l2(o_c, o) < 1e-12 and rel_l2(h_c, hT) < 1e-12
 
 
+def test_oracle_unit_selection_computes_exactly_the_listed_units():
+    """The oracle's `units` argument (evaluate only listed (sequence, value head) pairs):
+    every listed unit equals the same unit of a full run bit for bit, and the rows of
+    every unit not listed are left as the caller passed them (zeros here)."""
+    rng = np.random.default_rng(92)
+    lens = [21, 0, 37]
+    tot = sum(lens)
+    q, k, v, g, b, _ = _draw(rng, tot, 2, 6, 8, 5, glo=-1.0)
+    H0 = rng.standard_normal((len(lens), 6, 8, 5))
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    o, hT = oracle.serial_fwd(q, k, v, g, b, H0, seq_start=starts)
+    units = [(0, 5), (2, 0), (2, 3), (1, 4)]
+    o_u, h_u = oracle.serial_fwd(q, k, v, g, b, H0, seq_start=starts, units=units)
+    listed = set(units)
+    for n in range(len(lens)):
+        sl = slice(starts[n], starts[n + 1])
+        for h in range(6):
+            if (n, h) in listed:
+                assert np.array_equal(o_u[sl, h], o[sl, h])
+                assert np.array_equal(h_u[n, h], hT[n, h])
+            else:
+                assert not np.any(o_u[sl, h]) and not np.any(h_u[n, h])
+    with pytest.raises(ValueError):
+        oracle.serial_fwd(q, k, v, g, b, H0, seq_start=starts, units=[(3, 0)])
+    with pytest.raises(ValueError):
+        oracle.serial_fwd(q, k, v, g, b, H0, seq_start=starts, units=[(0, 6)])
+
+
 # ---------------------------------------------------------------- P10 -----
 def test_P10_channel_gate_constant_over_channels_equals_head_gate():
     rng = np.random.default_rng(101)
