@@ -178,6 +178,29 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same computation, kernels and launches as gdn_chunk_fwd with the composition
+ * gdn_plan_compose reports, but with no workspace argument: the workspace is the
+ * library's own array of GDN_NOALLOC_WORKSPACE_BYTES on each device, which the first
+ * call on a device looks up (no allocation) and which that device holds until the process
+ * ends.  Nothing is allocated or freed by any call.
+ *   p, q ... status, stream   as for gdn_chunk_fwd
+ * Every call on one device uses that device's one array: calls that overlap in time on a
+ * device (different streams or host threads) race and must be ordered by the caller.  The
+ * array keeps whatever the last call left; nothing in it needs clearing.
+ * Returns the codes of gdn_chunk_fwd, and GDN_E_WORKSPACE (nothing launched) when the
+ * problem's workspace (gdn_workspace_bytes of the resolved composition) exceeds
+ * GDN_NOALLOC_WORKSPACE_BYTES: e.g. the 32,768-token, 48-value-head layer pipelined needs
+ * about 39 MiB and fits; a 131,072-token packed batch does not.
+ */
+#define GDN_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* h0,
+                                 const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status,
+                                 void* stream);
+
+/*
  * gdn_decode_step -- one recurrent step: one new token for each of n_seq sequences,
  * continuing from their states (the hT of a prefill, or the h_out of an earlier step).
  * It is the same rule as above for a single token, evaluated directly:

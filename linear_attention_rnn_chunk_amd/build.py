@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn_mi355x.so")
-SOURCES = ["gdn_api.cpp", "gdn_kernels.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_kernels.hip", "gdn_decode.hip", "gdn_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 ALU forms are kept out of every code object

@@ -29,8 +29,10 @@ COMPOSE_AUTO, COMPOSE_SPLIT, COMPOSE_FUSED, COMPOSE_PIPELINED, COMPOSE_SEQSPLIT 
 STAGE_ALL, STAGE_PREP, STAGE_SCAN = 0, 1, 2
 
 # every symbol include/gdn.h declares
-EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_plan_compose", "gdn_chunk_fwd", "gdn_decode_step",
-           "gdn_error_string", "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_plan_compose", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc",
+           "gdn_decode_step", "gdn_error_string", "gdn_status_string", "gdn_abi_version")
+# the largest workspace gdn_chunk_fwd_noalloc serves (its per-device array)
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class Problem(ctypes.Structure):
@@ -81,6 +83,8 @@ def load():
             lib.gdn_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.c_size_t, vp]
             lib.gdn_chunk_fwd.restype = ctypes.c_int
+            lib.gdn_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
             lib.gdn_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.gdn_decode_step.restype = ctypes.c_int
             lib.gdn_error_string.argtypes = [ctypes.c_int32]
@@ -153,6 +157,17 @@ def chunk_fwd_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT, status
         ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
         _ptr(cu_seqlens), _ptr(o), _ptr(hT), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_bytes),
         ctypes.c_void_p(int(stream))))
+
+
+def chunk_fwd_noalloc_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT, status,
+                          stream=None) -> int:
+    """Direct call of gdn_chunk_fwd_noalloc (the library's own per-device workspace, no
+    allocation); returns the host code."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load().gdn_chunk_fwd_noalloc(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+        _ptr(cu_seqlens), _ptr(o), _ptr(hT), _ptr(status), ctypes.c_void_p(int(stream))))
 
 
 def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm: str = "bf16",
