@@ -502,6 +502,116 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_stamps(args):
+    """Per-phase step timestamps of one scan workgroup, from the measurement build
+    (libgdn_mi355x_stamps.so): the split composition's prep, then its scan with workgroup
+    --stamp-block recording kStampSteps chunk steps from the middle of its sequence.  Writes
+    the medians over steps and calls to profiles/scan_stamps_<config>.txt."""
+    import ctypes
+    import numpy as np
+    import torch
+
+    from linear_attention_rnn_chunk_amd import gdn, inputs
+    gdn.use_library(args.stamps_library or gdn.STAMPS_LIBRARY_PATH)
+    lib = gdn.load()
+    lib.gdn_debug_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+    lib.gdn_debug_stamps.restype = ctypes.c_int32
+    spec = inputs.CONFIGS[args.config]
+    chunk = args.chunk or spec.chunk
+    inp = inputs.make(spec)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def t(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    packed = spec.packed or len(set(spec.seq_lens)) > 1
+    B, Tn = (1, spec.tokens) if packed else (spec.n_seq, spec.seq_lens[0])
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if packed else None
+    shp = lambda a: a.reshape((B, Tn) + tuple(a.shape[1:]))
+    q, k, v, g, beta = (shp(t(getattr(inp, n))) for n in ("q", "k", "v", "g", "beta"))
+    h0 = t(inp.h0)
+    p_prep = layer_problem(args, spec, gdn.COMPOSE_SPLIT, gdn.STAGE_PREP)
+    p_scan = layer_problem(args, spec, gdn.COMPOSE_SPLIT, gdn.STAGE_SCAN)
+    o = torch.empty((B, Tn, spec.hv, spec.dv), dtype=torch.bfloat16 if args.arm == "bf16" else torch.float32,
+                    device=dev)
+    hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, gdn.workspace_bytes(p_prep)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    per = lib.gdn_debug_stamps(None, 0, 0)
+    NS, NK = 16, per // 16
+    nch = min((l + chunk - 1) // chunk for l in spec.seq_lens)
+    c0 = max(0, nch // 2 - NS // 2)
+    buf = torch.zeros(3 * NS * NK, dtype=torch.int64, device=dev)
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
+    runs, scan_ms = [], []
+    for rep in range(args.steps):
+        for prob, stamp in ((p_prep, False), (p_scan, True)):
+            lib.gdn_debug_stamps(ctypes.c_void_p(buf.data_ptr()) if stamp else None, args.stamp_block, c0)
+            if stamp:
+                buf.zero_()
+                if flush is not None:
+                    flush.fill_(rep & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            rc = gdn.chunk_fwd_raw(prob, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
+            if rc:
+                raise gdn.GdnError(rc, "gdn_chunk_fwd")
+            if stamp:
+                e1.record(stream)
+        torch.cuda.synchronize()
+        scan_ms.append(e0.elapsed_time(e1))
+        if rep >= 1:  # the first call sets the kernels' launch attributes
+            runs.append(buf.cpu().numpy().reshape(3, NS, NK).astype(np.int64))
+    lib.gdn_debug_stamps(None, 0, 0)
+    if int(status.item()):
+        raise gdn.GdnStatusError(int(status.item()))
+    a = np.stack(runs)  # [reps, role, step, phase]
+    med = lambda x: float(np.median(x))
+    chain, out, cpy = a[:, 0], a[:, 1], a[:, 2]
+    period = med(chain[:, 1:, 0] - chain[:, :-1, 0])
+    step_us = float(np.median(scan_ms)) * 1e3 / nch
+    rows = [("chain wave 0", [("Y = K H_in, X", chain[:, :-1, 1] - chain[:, :-1, 0]),
+                              ("R = T X, R S", chain[:, :-1, 2] - chain[:, :-1, 1]),
+                              ("state update, H_in of next", chain[:, :-1, 3] - chain[:, :-1, 2]),
+                              ("T loads issued, wait", chain[:, :-1, 4] - chain[:, :-1, 3]),
+                              ("barrier", chain[:, 1:, 0] - chain[:, :-1, 4])]),
+            ("output wave", [("loads, P R of previous chunk, stores", out[:, :-1, 1] - out[:, :-1, 0]),
+                             ("Q H_in of this chunk", out[:, :-1, 2] - out[:, :-1, 1]),
+                             ("wait for loads / stores", out[:, :-1, 3] - out[:, :-1, 2]),
+                             ("barrier", out[:, 1:, 0] - out[:, :-1, 3])]),
+            ("loader wave", [("copies issued", cpy[:, :-1, 1] - cpy[:, :-1, 0]),
+                             ("wait for the next chunk", cpy[:, :-1, 2] - cpy[:, :-1, 1]),
+                             ("gate sweep, V check", cpy[:, :-1, 3] - cpy[:, :-1, 2]),
+                             ("barrier", cpy[:, 1:, 0] - cpy[:, :-1, 3])])]
+    cmd = ("python -m linear_attention_rnn_chunk_amd.build --stamps && python3 <repo>/bench.py --stamps --config %s "
+           "--steps %d%s" % (args.config, args.steps, " --chunk %d" % args.chunk if args.chunk else ""))
+    lines = ["# scan step phases (shader-clock ticks, s_memtime) of workgroup %d, chunk steps %d..%d: %s"
+             % (args.stamp_block, c0, c0 + NS - 1, workload_title(args.config)),
+             "# command: " + cmd,
+             "# medians over %d steps x %d calls (cache-cold scan launches of the split composition)"
+             % (NS - 1, len(runs)),
+             "source_digest: %s" % source_digest("hybrid"),
+             "step_ticks: %.0f" % period,
+             "step_us: %.3f  (scan kernel %.4f ms / %d chunk steps)" % (step_us, float(np.median(scan_ms)), nch),
+             "ticks_per_us: %.0f" % (period / step_us)]
+    for role, phases in rows:
+        lines.append("%s:" % role)
+        for name, d in phases:
+            lines.append("  %-40s %7.0f" % (name, med(d)))
+    txt = "\n".join(lines) + "\n"
+    out = args.stamps_out or os.path.join(ROOT, "profiles", "scan_stamps_%s.txt" % args.config)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as f:
+        f.write(txt)
+    print(txt)
+
+
 def workload_title(name):
     spec = __import__("linear_attention_rnn_chunk_amd.inputs", fromlist=["CONFIGS"]).CONFIGS[name]
     seqs = ("B=%d, T=%d" % (spec.n_seq, spec.seq_lens[0]) if len(set(spec.seq_lens)) == 1 and not spec.packed
@@ -569,6 +679,13 @@ def main():
                     help="run only the warm-up and the timed calls (no per-stage pass, no warm-cache "
                          "pass): the form the profiling runs take, so every launch they see belongs "
                          "to one of warmup + steps whole-layer calls")
+    ap.add_argument("--stamps", action="store_true",
+                    help="per-phase step timestamps of one scan workgroup from the measurement build "
+                         "(python -m linear_attention_rnn_chunk_amd.build --stamps); writes "
+                         "profiles/scan_stamps_<config>.txt")
+    ap.add_argument("--stamp-block", type=int, default=0)
+    ap.add_argument("--stamps-library", default=None, help="another measurement build to load")
+    ap.add_argument("--stamps-out", default=None, help="write the summary here instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of MIB MiB three times "
                          "(reads and writes MIB MiB each): the reference for scaling HBM counters")
@@ -628,6 +745,8 @@ def main():
 
     if args.decode:
         return bench_decode(args)
+    if args.stamps:
+        return bench_stamps(args)
 
     spec = inputs.CONFIGS[args.config]
     chunk = args.chunk or spec.chunk

@@ -19,10 +19,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source into LIB (atomic replace).  Returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+# measurement build: the scan records per-phase step timestamps (gdn_debug_stamps)
+STAMPS_LIB = os.path.join(HERE, "libgdn_mi355x_stamps.so")
+
+
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    """Compile every HIP/C++ source into LIB (atomic replace), or with ``stamps`` the
+    measurement build into STAMPS_LIB.  Returns its path."""
+    lib = STAMPS_LIB if stamps else LIB
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = ([HIPCC] + FLAGS + (["-DGDN_SCAN_STAMPS"] if stamps else []) + [os.path.join(CSRC, s) for s in SOURCES]
+           + ["-o", tmp])
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and l.strip())
@@ -32,9 +39,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, out))
     if verbose and out:
         print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, stamps="--stamps" in sys.argv[1:]))

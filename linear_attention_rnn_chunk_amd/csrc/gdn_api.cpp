@@ -10,6 +10,12 @@
 
 namespace gdn {
 
+#ifdef GDN_SCAN_STAMPS
+// measurement build: where the next calls' scan records its step timestamps
+static uint64_t* g_stamps = nullptr;
+static int32_t g_stamp_block = 0, g_stamp_c0 = 0;
+#endif
+
 static inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 gdn_status make_plan(const gdn_problem* p, Plan* out) {
@@ -246,6 +252,11 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   prm.prep_ce = prm.seg_ce;
   prm.nscan = (int32_t)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
   prm.h0_input = 1;
+#ifdef GDN_SCAN_STAMPS
+  prm.stamps = gdn::g_stamps;
+  prm.stamp_block = gdn::g_stamp_block;
+  prm.stamp_c0 = gdn::g_stamp_c0;
+#endif
   if (ws && pl.seq_ok) {
     const size_t one = (size_t)gdn::kMaxParts * pl.n_seq * pl.hv * pl.dk * pl.dv;
     prm.Bws = (float*)(ws + pl.off_parts);
@@ -354,5 +365,18 @@ const char* gdn_status_string(uint32_t bits) {
 }
 
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+#ifdef GDN_SCAN_STAMPS
+// Measurement build only (not part of the ABI in include/gdn.h): the following calls' scan
+// workgroup `block` records, for kStampSteps chunk steps from chunk `c0`, a shader-clock
+// timestamp at each phase boundary of its chain wave 0, output wave and loader wave into
+// the device buffer `buf` ([3][kStampSteps][kStampPhases] uint64; NULL stops recording).
+int32_t gdn_debug_stamps(void* buf, int32_t block, int32_t c0) {
+  gdn::g_stamps = (uint64_t*)buf;
+  gdn::g_stamp_block = block;
+  gdn::g_stamp_c0 = c0;
+  return gdn::kStampSteps * gdn::kStampPhases;
+}
+#endif
 
 }  // extern "C"

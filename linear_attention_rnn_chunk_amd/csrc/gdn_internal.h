@@ -102,7 +102,13 @@ struct Params {
   float* Bws;
   float* Mws;
   float* Hws;
+  // Step timestamps of one scan workgroup, recorded only by a library built with
+  // GDN_SCAN_STAMPS (a measurement build): [3 roles: chain wave 0, output, loader]
+  // [kStampSteps steps from chunk stamp_c0][kStampPhases] shader-clock counts.
+  uint64_t* stamps;
+  int32_t stamp_block, stamp_c0;
 };
+constexpr int kStampSteps = 16, kStampPhases = 8;
 
 // Arguments of the one-token recurrent step (by value).
 struct DecodeParams {

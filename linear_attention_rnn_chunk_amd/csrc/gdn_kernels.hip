@@ -38,6 +38,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdlib.h>
+#include <string.h>
+
 #include <atomic>
 #include <type_traits>
 
@@ -1198,19 +1201,22 @@ __device__ __forceinline__ typename Arm::F kt_frag(const unsigned char* K, int s
   }
 }
 
-template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED>
+// The scan workgroup's LDS.  NCT: column tiles (of 16 state columns) per chain wave, so the
+// workgroup owns WC = 32 NCT state columns.
+template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED, int NCT = 1>
 struct ScanLds {
   typedef typename Arm::T T;
-  static constexpr int NBK = DK / 32, NBC = C / 32;
+  static constexpr int NBK = DK / 32, NBC = C / 32, WC = 32 * NCT;
   static constexpr int ESZV = QF32 ? 4 : 2;
   static constexpr int RND = 256, LDS_MAX = 160 * 1024;
   static constexpr int rnd(int x) { return (x + RND - 1) / RND * RND; }
   static constexpr int OPB = rnd(OpLayout<Arm, DK>::template bytes<C>());  // one C x DK operand
-  // exchange, double-buffered by chunk parity: H_in and R fragments of both chain waves
+  // exchange, double-buffered by chunk parity: H_in and R fragments of both chain waves'
+  // column tiles
   static constexpr int FRAG = 64 * 8 * (int)sizeof(T);
   static constexpr int HB = 0;
-  static constexpr int RO = HB + 2 * 2 * NBK * FRAG;
-  static constexpr int EXCH = RO + 2 * 2 * NBC * FRAG;
+  static constexpr int RO = HB + 2 * 2 * NCT * NBK * FRAG;
+  static constexpr int EXCH = RO + 2 * 2 * NCT * NBC * FRAG;
   static constexpr int TILEB = rnd(tile_elems(C) * (int)sizeof(T));  // T or P fragments of a chunk
   static constexpr int NDD = KDA ? (DK + 63) / 64 : 0;  // per-channel decay copies
   static constexpr int NSC = 4 * C + (KDA ? DK : 4);    // beta, beta e^G, e^{G_C-G}, e^G, decay
@@ -1227,16 +1233,23 @@ struct ScanLds {
   // (Measured for the split scan at dk = 128, C = 64: the slot layout with the copy wave
   // moving T and P is 1.5 % slower; giving up Q in the ring for a fourth buffer, 17 %.)
   static constexpr int base_bytes(bool qr) {
-    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * 32 * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256;
+    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * WC * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256;
   }
   static constexpr int FIXA = EXCH + 4 * TILEB + SSB;
   static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX;
   static constexpr int BUFA = base_bytes(QRA);
   static constexpr int NBUFA = 4 * BUFA + FIXA + 3 * SCB <= LDS_MAX ? 4
                                : (3 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 3 : (2 * BUFA + FIXA + 2 * SCB <= LDS_MAX ? 2 : 0));
-  static constexpr bool QRB = 2 * (base_bytes(true) + TILEB + SCB) + EXCH <= LDS_MAX;
+  // ring buffers of `buf` bytes that fit beside the exchange (at most 4; 0: not even 2)
+  static constexpr int nbuf_for(int buf) {
+    return 4 * buf + EXCH <= LDS_MAX ? 4 : (3 * buf + EXCH <= LDS_MAX ? 3 : (2 * buf + EXCH <= LDS_MAX ? 2 : 0));
+  }
+  // split: Q in the ring unless that leaves fewer buffers than Q out of it and fewer than 3
+  static constexpr int NQ_IN = nbuf_for(base_bytes(true) + TILEB + SCB);
+  static constexpr int NQ_OUT = nbuf_for(base_bytes(false) + TILEB + SCB);
+  static constexpr bool QRB = NQ_IN >= 3 || (NQ_IN >= 2 && NQ_IN == NQ_OUT);
   static constexpr int BUFB = base_bytes(QRB) + TILEB + SCB;
-  static constexpr int NBUFB = 4 * BUFB + EXCH <= LDS_MAX ? 4 : (3 * BUFB + EXCH <= LDS_MAX ? 3 : 2);
+  static constexpr int NBUFB = QRB ? NQ_IN : NQ_OUT;
   static constexpr bool TL = FUSED;
   static_assert(!FUSED || NBUFA >= 2, "fused scan LDS budget");
   // Q goes through the ring (copied like K, read from LDS by the output wave) when two
@@ -1252,7 +1265,7 @@ struct ScanLds {
   static constexpr int QO = KH + OPB;
   static constexpr int PP = QO + (QR ? OPB : 0);      // !TL: P fragments
   static constexpr int VV = PP + (TL ? 0 : TILEB);
-  static constexpr int GX = VV + rnd(C * 32 * ESZV);  // gate rows (per-head gate)
+  static constexpr int GX = VV + rnd(C * WC * ESZV);  // gate rows (per-head gate)
   static constexpr int GB = GX + (KDA ? 0 : 256);     // beta rows
   static constexpr int DC = GB + 256;                 // e^{G_C} per key channel
   static constexpr int SC = DC + NDD * 256;           // !TL: row scalars
@@ -1269,19 +1282,45 @@ struct ScanLds {
   // loader copy instructions per chunk
   static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;
   static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;  // T or P of a chunk
-  static constexpr int NDV = C * 32 * ESZV / 1024;
+  static constexpr int NDV = C * WC * ESZV / 1024;
   static constexpr int ND = ((KDA ? 2 : 1) + (QR ? 1 : 0)) * NDK + (TL ? 0 : NDT) + NDV + (KDA ? 1 : 2) + NDD;
   static_assert(NDK * 1024 == OpLayout<Arm, DK>::template bytes<C>(), "K copy granularity");
   static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "T / P copy granularity");
-  static_assert(NDV * 1024 == C * 32 * ESZV, "V copy granularity");
+  static_assert(NDV * 1024 == C * WC * ESZV, "V copy granularity");
+  static_assert(!FUSED || NCT == 1, "fused composition: 32 state columns per workgroup");
 };
 
-template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED>
+#ifndef GDN_WIDE_SCAN
+#define GDN_WIDE_SCAN 1
+#endif
+
+// Measurement build (GDN_SCAN_STAMPS): role r's shader-clock count at phase k of chunk step
+// ci, from lane 0 of workgroup stamp_block, for steps stamp_c0 .. stamp_c0 + kStampSteps - 1
+// (r: 0 chain wave 0, 1 output wave, 2 loader).  The scheduling barriers keep the count where
+// it stands in program order; a phase that ends with a use of a matrix product's result
+// therefore records when that result was ready.  The product library records nothing.
+#ifdef GDN_SCAN_STAMPS
+#define GDN_STAMP(r, ci, k)                                                                            \
+  do {                                                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
+    if (p.stamps && (int)blockIdx.x == p.stamp_block && (ci) >= p.stamp_c0 &&                          \
+        (ci) < p.stamp_c0 + kStampSteps && lane == 0)                                                  \
+      p.stamps[((r) * kStampSteps + (ci) - p.stamp_c0) * kStampPhases + (k)] = __builtin_amdgcn_s_memtime(); \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
+  } while (0)
+#else
+#define GDN_STAMP(r, ci, k) \
+  do {                      \
+  } while (0)
+#endif
+
+template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED, int NCT = 1>
 __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
   using Lay = OpLayout<Arm, DK>;
-  using SL = ScanLds<Arm, DK, C, KDA, QF32, FUSED>;
+  using SL = ScanLds<Arm, DK, C, KDA, QF32, FUSED, NCT>;
+  constexpr int WC = SL::WC;  // state columns of this workgroup
   static_assert(!FUSED || (!KDA && !QF32), "fused composition: per-head gate, bf16 inputs");
   if constexpr (!KDA && !FUSED) {
     if ((int)blockIdx.x >= p.nscan) {  // pipelined composition: the next segment's prep
@@ -1300,7 +1339,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   // to the SIMDs round-robin, so in the fused workgroup the chain waves take waves 2 and 3
   // (SIMDs of their own) and the tile waves share SIMDs with the output and loader waves.
   const int role = FUSED ? (wave < 4 ? (wave + 2) & 3 : wave) : wave;
-  const int DV = p.dv, nslice = DV / 32;
+  const int DV = p.dv, nslice = DV / WC;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  With
   // key heads a multiple of 8, XCD x = blockIdx % 8 takes key heads x, x + 8, ... of
   // every sequence, sequence by sequence: the workgroups reading one key head share an
@@ -1369,11 +1408,11 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     if constexpr (SL::TL) return (float*)(exch + SL::SCR + (ci % SL::NSCS) * SL::SCB);
     else return (float*)(bufp(ci) + SL::SC);
   };
-  auto hb_at = [&](int par, int u, int kb) __attribute__((always_inline)) {
-    return (T*)(exch + SL::HB + ((par * 2 + u) * NBK + kb) * SL::FRAG) + lane * 8;
+  auto hb_at = [&](int par, int u, int c, int kb) __attribute__((always_inline)) {
+    return (T*)(exch + SL::HB + (((par * 2 + u) * NCT + c) * NBK + kb) * SL::FRAG) + lane * 8;
   };
-  auto ro_at = [&](int par, int u, int sb) __attribute__((always_inline)) {
-    return (T*)(exch + SL::RO + ((par * 2 + u) * NBC + sb) * SL::FRAG) + lane * 8;
+  auto ro_at = [&](int par, int u, int c, int sb) __attribute__((always_inline)) {
+    return (T*)(exch + SL::RO + (((par * 2 + u) * NCT + c) * NBC + sb) * SL::FRAG) + lane * 8;
   };
   // operand sources: row-major rows of DK arm elements, `ld` elements apart
   const int64_t hvs = (int64_t)p.hv;
@@ -1400,7 +1439,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // the waits below are exact.
     // per-lane byte offsets of this lane's pieces inside a full chunk (fixed), so that each
     // copy of a full chunk is a uniform base plus a 32-bit offset
-    constexpr int VPR = 32 * ESZV / 16;  // pieces per V row
+    constexpr int VPR = WC * ESZV / 16;  // pieces per V row
     uint32_t koff[SL::NDK], voff[SL::NDV];
 #pragma unroll
     for (int k = 0; k < SL::NDK; ++k) {
@@ -1417,7 +1456,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       unsigned char* B = bufp(ci);
       const int64_t t0 = chunk_t0(ci);
       const int L = chunk_L(ci);
-      const char* vsrc = (const char*)p.v + (t0 * hvs + h) * (int64_t)(DV * ESZV) + 32 * slice * ESZV;
+      const char* vsrc = (const char*)p.v + (t0 * hvs + h) * (int64_t)(DV * ESZV) + WC * slice * ESZV;
       if (L == C) {  // uniform
 #pragma unroll
         for (int w = 0; w < (KDA ? 2 : 1) + (SL::QR ? 1 : 0); ++w) {
@@ -1511,14 +1550,18 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       if (j < nch) sweep(j);
     copy_wave_barrier();
     for (int ci = 0; ci < nch; ++ci) {
+      GDN_STAMP(2, ci, 0);
       const bool more = ci + LA < nch;
       if (more) issue(ci + LA);
+      GDN_STAMP(2, ci, 1);
       // chunk ci + CL complete: all copies but this step's, which stay in flight across
       // the barrier
       if (LA > CL && more) wait_vm<(LA > CL ? SL::ND : 0)>();
       else wait_vm<0>();
+      GDN_STAMP(2, ci, 2);
       if (ci + CL < nch) sweep(ci + CL);
       check_v(ci);
+      GDN_STAMP(2, ci, 3);
       copy_wave_barrier();
     }
   } else if (role == 2) {
@@ -1569,73 +1612,84 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       else f = Arm::ld8((const T*)raw);
       return f;
     };
-    f32x4 OQ[2][NT];  // e^G (Q H_in) of the chunk in flight, both column halves
+    f32x4 OQ[2][NCT][NT];  // e^G (Q H_in) of the chunk in flight, every column tile
     auto out_q = [&](int ci, int set) __attribute__((always_inline)) {
       const int par = ci & 1;
       const float* S = scal(ci);
       const unsigned char* Qb = bufp(ci) + SL::QO;
+      float e[NT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        F hb[NBK];
+      for (int nt = 0; nt < NT; ++nt) e[nt] = KDA ? 1.f : S[3 * C + 16 * nt + i];
 #pragma unroll
-        for (int kb = 0; kb < NBK; ++kb) hb[kb] = Arm::ld8(hb_at(par, u, kb));
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f32x4 o = zero4();
+        for (int c = 0; c < NCT; ++c) {
+          F hb[NBK];
 #pragma unroll
-          for (int kb = 0; kb < NBK; ++kb) {
-            F qf;
-            if constexpr (SL::QR) qf = Lay::ld8(Qb, 16 * nt + i, 32 * kb + 8 * g);
-            else qf = frag(qr[set][SL::QR ? 0 : nt][kb]);
-            o = Arm::mma(hb[kb], qf, o);
+          for (int kb = 0; kb < NBK; ++kb) hb[kb] = Arm::ld8(hb_at(par, u, c, kb));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            f32x4 o = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NBK; ++kb) {
+              F qf;
+              if constexpr (SL::QR) qf = Lay::ld8(Qb, 16 * nt + i, 32 * kb + 8 * g);
+              else qf = frag(qr[set][SL::QR ? 0 : nt][kb]);
+              o = Arm::mma(hb[kb], qf, o);
+            }
+            OQ[u][c][nt] = o * e[nt];
           }
-          const float e = KDA ? 1.f : S[3 * C + 16 * nt + i];
-          OQ[u][nt] = o * e;
         }
-      }
     };
     auto out_p = [&](int ci, int set) __attribute__((always_inline)) {  // finish chunk ci
       const int par = ci & 1;
       const int64_t t0 = chunk_t0(ci);
       const int L = chunk_L(ci);
       // all products first (independent accumulators), then checks and stores
-      f32x4 o[2][NT];
+      f32x4 o[2][NCT][NT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        F ro[NBC];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int sb = 0; sb < NBC; ++sb) ro[sb] = Arm::ld8(ro_at(par, u, sb));
+        for (int c = 0; c < NCT; ++c) {
+          F ro[NBC];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          o[u][nt] = OQ[u][nt];
+          for (int sb = 0; sb < NBC; ++sb) ro[sb] = Arm::ld8(ro_at(par, u, c, sb));
 #pragma unroll
-          for (int sb = 0; sb < NBC; ++sb)
-            if (32 * sb <= 16 * nt + 15) o[u][nt] = Arm::mma(ro[sb], frag(pr[set][sb][nt]), o[u][nt]);
+          for (int nt = 0; nt < NT; ++nt) {
+            o[u][c][nt] = OQ[u][c][nt];
+#pragma unroll
+            for (int sb = 0; sb < NBC; ++sb)
+              if (32 * sb <= 16 * nt + 15) o[u][c][nt] = Arm::mma(ro[sb], frag(pr[set][sb][nt]), o[u][c][nt]);
+          }
         }
-      }
       // Inf/NaN in any row (rows past a partial chunk's end repeat finite inputs, so they
       // are nonfinite only together with a real row)
       uint32_t nf = 0;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int c = 0; c < NCT; ++c)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) nf |= (__float_as_uint(o[u][nt][j]) & 0x7F800000u) + 0x00800000u;
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) nf |= (__float_as_uint(o[u][c][nt][j]) & 0x7F800000u) + 0x00800000u;
       bad |= flag_if(nf & 0x80000000u, GDN_ST_NONFINITE_OUTPUT);
       // rows of this chunk: uniform base plus the lane's fixed row offsets
-      char* ob = (char*)p.o + ((t0 * hvs + h) * (int64_t)DV + 32 * slice) * OSZ;
-      // lane (i, g) of tile nt holds row 16 nt + i, slice columns 8 g .. 8 g + 7 (the
+      char* ob = (char*)p.o + ((t0 * hvs + h) * (int64_t)DV + WC * slice) * OSZ;
+      // lane (i, g) of tile (nt, c) holds row 16 nt + i, slice columns 32 c + 8 g .. + 7 (the
       // first four from chain wave 0's quad, the next four from wave 1's)
       auto st = [&](int nt) __attribute__((always_inline)) {
-        char* a = ob + ooff[nt];
-        const f32x4 v0 = o[0][nt], v1 = o[1][nt];
-        if (OSZ == 4) {
-          *(float4*)a = (float4){v0[0], v0[1], v0[2], v0[3]};
-          *(float4*)(a + 16) = (float4){v1[0], v1[1], v1[2], v1[3]};
-        } else {
-          const uint2 w0 = pack_bf16x4(v0), w1 = pack_bf16x4(v1);
-          *(u32x4*)a = (u32x4){w0.x, w0.y, w1.x, w1.y};
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          char* a = ob + ooff[nt] + 32 * c * OSZ;
+          const f32x4 v0 = o[0][c][nt], v1 = o[1][c][nt];
+          if (OSZ == 4) {
+            *(float4*)a = (float4){v0[0], v0[1], v0[2], v0[3]};
+            *(float4*)(a + 16) = (float4){v1[0], v1[1], v1[2], v1[3]};
+          } else {
+            const uint2 w0 = pack_bf16x4(v0), w1 = pack_bf16x4(v1);
+            *(u32x4*)a = (u32x4){w0.x, w0.y, w1.x, w1.y};
+          }
         }
       };
       if (L == C) {
@@ -1658,13 +1712,17 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // sets alternate by chunk parity; the loop is unrolled by two so they are constants.
     auto ostep = [&](auto PAR, int ci) __attribute__((always_inline)) {
       constexpr int cur = decltype(PAR)::value;  // ci & 1
+      GDN_STAMP(1, ci, 0);
       // prefetches first; they complete before the barrier, so no load is outstanding
       // across steps and the products below never wait on memory
       if (ci + 1 < nch) load_q(ci + 1, SL::QR ? 0 : cur ^ 1);
       load_p(ci, cur);
       if (ci > 0) out_p(ci - 1, cur ^ 1);
+      GDN_STAMP(1, ci, 1);
       out_q(ci, SL::QR ? 0 : cur);
-      if constexpr (!SL::QR) wait_vm<0>();  // Q loads (stores are never waited on)
+      GDN_STAMP(1, ci, 2);
+      if constexpr (!SL::QR) wait_vm<0>();  // Q loads (and this step's stores)
+      GDN_STAMP(1, ci, 3);
       __syncthreads();
     };
     int ci = 0;  // whole pairs, then a last odd step (as in the chain loop)
@@ -1679,11 +1737,14 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     }
   } else if (role < 2) {
     // -------------------------------------------------------------- chain ----
+    // Each chain wave owns NCT column tiles of 16 state columns; the K fragments of a chunk
+    // (rows for Y = K H, transposed for the state update) and T serve all of them.
     const int u = role;
-    // this lane's state column inside the slice: the two chain waves own interleaved
-    // quads, so the output wave holds 8 consecutive columns of a row per lane
-    const int ccol = 8 * (i >> 2) + 4 * u + (i & 3);
-    const int col0 = 32 * slice + ccol;
+    // this lane's state column in column tile c of the slice: the two chain waves own
+    // interleaved quads of each 32 columns, so the output wave holds 8 consecutive columns
+    // of a row per lane
+    auto ccol = [&](int c) __attribute__((always_inline)) { return 32 * c + 8 * (i >> 2) + 4 * u + (i & 3); };
+    const int col0 = WC * slice + ccol(0);  // column tile c: col0 + 32 c
     // this workgroup's starting state and where its final state goes ([dk][dv] fp32 each)
     const int64_t hsz = DK * (int64_t)DV, hbase = ((int64_t)n * p.hv + h) * hsz;
     const float* hin = p.h0 ? p.h0 + hbase : nullptr;
@@ -1697,27 +1758,34 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       hout = kind == 0 ? p.Bws + pt : (kind == 1 ? p.Mws + pt : (part == p.nparts - 1 && p.hT ? p.hT + real : nullptr));
       hcheck = kind == 0 && part == 0;
     }
-    f32x4 H[NTK];
+    f32x4 H[NCT][NTK];
     if (hin) {
 #pragma unroll
-      for (int t = 0; t < NTK; ++t)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          H[t][j] = hin[(int64_t)state_dim(t, g, j) * DV + col0];
-          bad |= flag_if(hcheck && f_nonfinite(H[t][j]), GDN_ST_NONFINITE_INPUT);
-        }
+        for (int t = 0; t < NTK; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            H[c][t][j] = hin[(int64_t)state_dim(t, g, j) * DV + col0 + 32 * c];
+            bad |= flag_if(hcheck && f_nonfinite(H[c][t][j]), GDN_ST_NONFINITE_INPUT);
+          }
     } else {
 #pragma unroll
-      for (int t = 0; t < NTK; ++t)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) H[t][j] = (PARTS && kind == 1 && state_dim(t, g, j) == col0) ? 1.f : 0.f;
-    }
-    F HB[NBK];
+        for (int t = 0; t < NTK; ++t)
 #pragma unroll
-    for (int kb = 0; kb < NBK; ++kb) {
-      HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
-      Arm::st8(hb_at(0, u, kb), H[2 * kb], H[2 * kb + 1]);
+          for (int j = 0; j < 4; ++j)
+            H[c][t][j] = (PARTS && kind == 1 && state_dim(t, g, j) == col0 + 32 * c) ? 1.f : 0.f;
     }
+    F HB[NCT][NBK];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NBK; ++kb) {
+        HB[c][kb] = Arm::acc(H[c][2 * kb], H[c][2 * kb + 1]);
+        Arm::st8(hb_at(0, u, c, kb), H[c][2 * kb], H[c][2 * kb + 1]);
+      }
     F kf[NBK][NT];  // K row fragments of the chunk being processed
     // T fragments: straight from global memory (stored in exactly this layout), two chunks
     // ahead into two register sets (set = chunk parity); the chain issues no other global
@@ -1760,18 +1828,21 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       const unsigned char* B = bufp(ci);
       const float* S = scal(ci);
       const int par = ci & 1;
+      if (u == 0) GDN_STAMP(0, ci, 0);
       if (!PRE) load_kf(ci);
       // operands of the rest of this chunk, read (after K) while the products run
-      float vv[NT][4];
+      float vv[NCT][NT][4];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * mt + 4 * g + j;
-          if constexpr (QF32) vv[mt][j] = *(const float*)(B + SL::VV + (r * 32 + ccol) * 4);
-          else vv[mt][j] = bf2f(*(const uint16_t*)(B + SL::VV + (r * 32 + ccol) * 2));
-          if (vzero) vv[mt][j] = 0.f;
-        }
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 16 * mt + 4 * g + j;
+            if constexpr (QF32) vv[c][mt][j] = *(const float*)(B + SL::VV + (r * WC + ccol(c)) * 4);
+            else vv[c][mt][j] = bf2f(*(const uint16_t*)(B + SL::VV + (r * WC + ccol(c)) * 2));
+            if (vzero) vv[c][mt][j] = 0.f;
+          }
       float4 b4[NT], e4[NT];
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
@@ -1790,13 +1861,17 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
             else tf[sb][mt] = Arm::ld8((const T*)tr_[sb][mt]);
           }
       // Y = K H_in
-      f32x4 Y[NT];
+      f32x4 Y[NCT][NT];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) Y[mt] = zero4();
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) Y[c][mt] = zero4();
 #pragma unroll
       for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt) Y[mt] = Arm::mma(kf[kb][mt], HB[kb], Y[mt]);
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) Y[c][mt] = Arm::mma(kf[kb][mt], HB[c][kb], Y[c][mt]);
       // transposed K fragments for the state update, read while the products run
       F ktf[NBC][NTK];
 #pragma unroll
@@ -1805,80 +1880,102 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int t = 0; t < NTK; ++t) ktf[sb][t] = kt_frag<Arm, DK>(B + SL::KH, sb, t, lane);
       // e^{G_C} H_in (the state's old part), off the product chain
 #pragma unroll
-      for (int t = 0; t < NTK; ++t) {
-        if constexpr (KDA) {
-          const float4 d4 = *(const float4*)(S + 4 * C + state_dim(t, g, 0));
-          H[t][0] *= d4.x; H[t][1] *= d4.y; H[t][2] *= d4.z; H[t][3] *= d4.w;
-        } else {
-          const float d = S[4 * C];
-          H[t][0] *= d; H[t][1] *= d; H[t][2] *= d; H[t][3] *= d;
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int t = 0; t < NTK; ++t) {
+          if constexpr (KDA) {
+            const float4 d4 = *(const float4*)(S + 4 * C + state_dim(t, g, 0));
+            H[c][t][0] *= d4.x; H[c][t][1] *= d4.y; H[c][t][2] *= d4.z; H[c][t][3] *= d4.w;
+          } else {
+            const float d = S[4 * C];
+            H[c][t][0] *= d; H[c][t][1] *= d; H[c][t][2] *= d; H[c][t][3] *= d;
+          }
         }
-      }
       __builtin_amdgcn_sched_barrier(0);
       // next chunk's K fragments (its buffer is complete one barrier early)
       if (PRE && ci + 1 < nch) load_kf(ci + 1);
       // X = beta V - beta e^G Y  (per-channel gate: K carries e^G, X = beta (V - Y))
-      F XB[NBC];
-      {
+      F XB[NCT][NBC];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
         f32x4 X[NT];
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
           const float bv[4] = {b4[mt].x, b4[mt].y, b4[mt].z, b4[mt].w};
           if constexpr (KDA) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) X[mt][j] = bv[j] * (vv[mt][j] - Y[mt][j]);
+            for (int j = 0; j < 4; ++j) X[mt][j] = bv[j] * (vv[c][mt][j] - Y[c][mt][j]);
           } else {
             const float ev[4] = {e4[mt].x, e4[mt].y, e4[mt].z, e4[mt].w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) X[mt][j] = bv[j] * vv[mt][j] - ev[j] * Y[mt][j];
+            for (int j = 0; j < 4; ++j) X[mt][j] = bv[j] * vv[c][mt][j] - ev[j] * Y[c][mt][j];
           }
         }
 #pragma unroll
-        for (int sb = 0; sb < NBC; ++sb) XB[sb] = Arm::acc(X[2 * sb], X[2 * sb + 1]);
+        for (int sb = 0; sb < NBC; ++sb) XB[c][sb] = Arm::acc(X[2 * sb], X[2 * sb + 1]);
       }
+      if (u == 0) GDN_STAMP(0, ci, 1);  // Y = K H_in ready (X formed from it)
       // R = T X
-      f32x4 R[NT];
+      f32x4 R[NCT][NT];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) R[mt] = zero4();
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) R[c][mt] = zero4();
 #pragma unroll
       for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt)
-          if (32 * sb <= 16 * mt + 15) R[mt] = Arm::mma(tf[sb][mt], XB[sb], R[mt]);
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt)
+            if (32 * sb <= 16 * mt + 15) R[c][mt] = Arm::mma(tf[sb][mt], XB[c][sb], R[c][mt]);
       __builtin_amdgcn_sched_barrier(0);
       // R for the output wave; e^{G_C - G} R for the state update (per-channel gate: the
       // factor is inside Ktil)
-      F RS[NBC];
+      F RS[NCT][NBC];
 #pragma unroll
       for (int sb = 0; sb < NBC; ++sb) {
-        Arm::st8(ro_at(par, u, sb), R[2 * sb], R[2 * sb + 1]);
-        if constexpr (KDA) {
-          RS[sb] = Arm::acc(R[2 * sb], R[2 * sb + 1]);
-        } else {
-          const float4 a = *(const float4*)(S + 2 * C + 32 * sb + 4 * g);
-          const float4 c = *(const float4*)(S + 2 * C + 32 * sb + 16 + 4 * g);
-          f32x4 lo = R[2 * sb], hi = R[2 * sb + 1];
-          lo[0] *= a.x; lo[1] *= a.y; lo[2] *= a.z; lo[3] *= a.w;
-          hi[0] *= c.x; hi[1] *= c.y; hi[2] *= c.z; hi[3] *= c.w;
-          RS[sb] = Arm::acc(lo, hi);
+        float4 a = {0.f, 0.f, 0.f, 0.f}, cc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!KDA) {
+          a = *(const float4*)(S + 2 * C + 32 * sb + 4 * g);
+          cc = *(const float4*)(S + 2 * C + 32 * sb + 16 + 4 * g);
+        }
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          Arm::st8(ro_at(par, u, c, sb), R[c][2 * sb], R[c][2 * sb + 1]);
+          if constexpr (KDA) {
+            RS[c][sb] = Arm::acc(R[c][2 * sb], R[c][2 * sb + 1]);
+          } else {
+            f32x4 lo = R[c][2 * sb], hi = R[c][2 * sb + 1];
+            lo[0] *= a.x; lo[1] *= a.y; lo[2] *= a.z; lo[3] *= a.w;
+            hi[0] *= cc.x; hi[1] *= cc.y; hi[2] *= cc.z; hi[3] *= cc.w;
+            RS[c][sb] = Arm::acc(lo, hi);
+          }
         }
       }
+      if (u == 0) GDN_STAMP(0, ci, 2);  // R = T X ready (R stored, R S formed)
       // H <- e^{G_C} H_in + Ktil^T R
 #pragma unroll
       for (int sb = 0; sb < NBC; ++sb)
 #pragma unroll
-        for (int t = 0; t < NTK; ++t) H[t] = Arm::mma(ktf[sb][t], RS[sb], H[t]);
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int t = 0; t < NTK; ++t) H[c][t] = Arm::mma(ktf[sb][t], RS[c][sb], H[c][t]);
       // H_in of the next chunk, for this wave and for the output wave
 #pragma unroll
-      for (int kb = 0; kb < NBK; ++kb) {
-        HB[kb] = Arm::acc(H[2 * kb], H[2 * kb + 1]);
-        Arm::stf(hb_at(par ^ 1, u, kb), HB[kb]);
-      }
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int kb = 0; kb < NBK; ++kb) {
+          HB[c][kb] = Arm::acc(H[c][2 * kb], H[c][2 * kb + 1]);
+          Arm::stf(hb_at(par ^ 1, u, c, kb), HB[c][kb]);
+        }
+      if (u == 0) GDN_STAMP(0, ci, 3);  // state update ready (H_in of the next chunk formed)
       // chunk ci + 2's T into this chunk's set; chunk ci + 1's (issued a step ago) must be
       // complete at the barrier, chunk ci + 2's may stay in flight.  (The compiler also
-      // waits for the newest set before R = T X, since it merges the two branches below
-      // along a path that cannot occur; loading unconditionally removes that wait, which
-      // measured 2 % faster at chunk 32 but 2 % slower at chunk 64, so the branch stays.)
+      // waits for the newest set before R = T X in the first step of each pair, since it
+      // merges its wait-count state across the two branches below; loading unconditionally
+      // removes that wait but measured 1 % slower on the hybrid layer, and loading three
+      // chunks ahead, which also shortens the wait below, measured the same: the step is
+      // then bounded by the other waves' share of the CU, not by the T loads.)
       if constexpr (!SL::TL) {
         if (ci + 2 < nch) {
           load_t(ci + 2, PAR);
@@ -1887,6 +1984,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           wait_vm<0>();
         }
       }
+      if (u == 0) GDN_STAMP(0, ci, 4);
       __syncthreads();
     };
     // whole pairs of steps, then a last odd step (no step skipped inside the loop body)
@@ -1898,12 +1996,14 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     if (ci < nch) cstep(std::integral_constant<int, 0>{}, ci);
     if (hout) {
 #pragma unroll
-      for (int t = 0; t < NTK; ++t)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bad |= flag_if(f_nonfinite(H[t][j]), GDN_ST_NONFINITE_OUTPUT);
-          hout[(int64_t)state_dim(t, g, j) * DV + col0] = H[t][j];
-        }
+        for (int t = 0; t < NTK; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bad |= flag_if(f_nonfinite(H[c][t][j]), GDN_ST_NONFINITE_OUTPUT);
+            hout[(int64_t)state_dim(t, g, j) * DV + col0 + 32 * c] = H[c][t][j];
+          }
     }
   } else if constexpr (FUSED) {
     // ------------------------------------------------------ tiles (fused) ----
@@ -2012,11 +2112,32 @@ bool set_lds_once(Fn fn, size_t lds) {
   return true;
 }
 
+// State columns of one scan workgroup: 32, or 64 (two column tiles per chain wave, so a
+// chunk's K, Q, T and P, fetched and staged once per workgroup, serve twice the columns)
+// when 32-column workgroups would need more than one round of the device's compute units
+// (bf16 arm, dv a multiple of 64, not fused).  Measured (scan kernel, same box): the packed
+// 131,072-token batch 2.38 -> 2.18 ms with 64 columns (384 workgroups instead of 768); the
+// hybrid layer 0.77 -> 1.02 ms and the per-channel layer 0.44 -> 0.50 ms, where 32 columns
+// already fit in one round: a 64-column step is about 1.65x as long (the chain waves twice
+// the products) and half as many units run.
+// GDN_SCAN_COLUMNS=32 or 64 in the environment overrides the rule where 64 is possible (the
+// tests compare the two widths on one problem).
+int scan_cols(const Plan& pl) {
+  if (!GDN_WIDE_SCAN || pl.arm_f32 || pl.fused || pl.dv % 64 != 0) return 32;
+  if (const char* e = getenv("GDN_SCAN_COLUMNS")) {
+    if (!strcmp(e, "32")) return 32;
+    if (!strcmp(e, "64")) return 64;
+  }
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 32;
+  return (int64_t)pl.n_seq * pl.hv * (pl.dv / 32) > ncu ? 64 : 32;
+}
+
 // Pipelined composition: the scan in chunk-aligned segments of kSegTokens tokens (the
 // state carried in `carry`), each launch also running the next segment's prep in
 // workgroups after the scan's own.
-
-template <class Arm, int DK, int C, bool QF32>
+template <class Arm, int DK, int C, bool QF32, int NCT>
 gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int nprep, hipStream_t st) {
   constexpr int SEG = kSegTokens / C;  // chunks per segment
   const int cps = pl.chunks_per_seq;
@@ -2024,8 +2145,8 @@ gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int np
   auto cut = [&](int s) { return s < S ? s * SEG : cps; };
   const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
   if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
-  using SL = ScanLds<Arm, DK, C, false, QF32, false>;
-  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false>, SL::BYTES)) return GDN_E_LAUNCH;
+  using SL = ScanLds<Arm, DK, C, false, QF32, false, NCT>;
+  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false, NCT>, SL::BYTES)) return GDN_E_LAUNCH;
   Params q = prm;
   q.tile_ring = pl.tile_ring;  // (the plan's ring half is one segment, SEG chunks)
   q.prep_cb = 0;
@@ -2046,7 +2167,8 @@ gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int np
     q.h0_input = s == 0;
     q.hT = last ? prm.hT : carry;
     const int grid = q.nscan + (last ? 0 : nprep);
-    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false>), dim3((unsigned)grid), dim3(256), SL::BYTES, st, q);
+    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false, NCT>), dim3((unsigned)grid), dim3(256), SL::BYTES,
+                       st, q);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   return GDN_OK;
@@ -2089,43 +2211,50 @@ int seqsplit_parts(const Plan& pl, int nscan) {
   return parts < 2 ? 2 : parts;
 }
 
-template <class Arm, int DK, int C, bool QF32>
+template <class Arm, int DK, int C, bool QF32, int NCT>
 gdn_status run_seqsplit(const Plan& pl, const Params& prm, int parts, hipStream_t st) {
   const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
   if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
-  using SL = ScanLds<Arm, DK, C, false, QF32, false>;
-  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false>, SL::BYTES)) return GDN_E_LAUNCH;
+  using SL = ScanLds<Arm, DK, C, false, QF32, false, NCT>;
+  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false, NCT>, SL::BYTES)) return GDN_E_LAUNCH;
   hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)((pl.max_slots + 7) / 8 * 8 * pl.hk * nblk)),
                      dim3(64 * wpb), wpb * SolveLds<C>::FLOATS * sizeof(float), st, prm);
   if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
-  const int per = pl.hv * (pl.dv / 32);  // scan workgroups per (virtual) sequence
+  const int per = pl.hv * (pl.dv / SL::WC);  // scan workgroups per (virtual) sequence
   Params q = prm;
   q.pmode = 1;
   q.nparts = parts;
   q.part_chunks = (pl.chunks_per_seq + parts - 1) / parts;
   q.pvirt = 2 * parts - 2;  // every part's own state, the inner parts' transitions
   q.nscan = pl.n_seq * q.pvirt * per;
-  hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false>), dim3((unsigned)q.nscan), dim3(256), SL::BYTES, st, q);
+  hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false, NCT>), dim3((unsigned)q.nscan), dim3(256), SL::BYTES,
+                     st, q);
   if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
+  // the chain kernel's own grid: 32-column slices of every state
+  const int per32 = pl.hv * (pl.dv / 32);
   for (int step = 1; step + 1 < parts; ++step) {  // chain: H_{step+1} = M_step H_step + B_step
-    hipLaunchKernelGGL(gdn_seq_chain, dim3((unsigned)(pl.n_seq * per * (DK / 32))), dim3(256), 0, st, q, DK, step);
+    hipLaunchKernelGGL(gdn_seq_chain, dim3((unsigned)(pl.n_seq * per32 * (DK / 32))), dim3(256), 0, st, q, DK, step);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   q.pmode = 2;
   q.pvirt = parts - 1;  // the parts after the first, from their chained states
   q.nscan = pl.n_seq * q.pvirt * per;
-  hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false>), dim3((unsigned)q.nscan), dim3(256), SL::BYTES, st, q);
+  hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false, NCT>), dim3((unsigned)q.nscan), dim3(256), SL::BYTES,
+                     st, q);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_E_LAUNCH;
 }
 
-template <class Arm, int DK, int C, bool KDA, bool QF32>
-gdn_status run(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
+template <class Arm, int DK, int C, bool KDA, bool QF32, int NCT>
+gdn_status run_cols(const Plan& pl, const Params& prm0, void* carry, hipStream_t st) {
+  Params prm = prm0;
+  prm.nscan = (int32_t)((int64_t)pl.n_seq * pl.hv * (pl.dv / (32 * NCT)));
   if constexpr (!KDA) {  // the same decisions as plan_compose()
     const int nprep = pipelined_prep_wgs(pl, prm.nscan);
     if (nprep > 0 && pl.run_prep && pl.run_scan && pl.max_slots > 0)
-      return run_pipelined<Arm, DK, C, QF32>(pl, prm, (float*)carry, nprep, st);
+      return run_pipelined<Arm, DK, C, QF32, NCT>(pl, prm, (float*)carry, nprep, st);
     const int parts = seqsplit_parts(pl, prm.nscan);
-    if (parts > 0 && pl.run_prep && pl.run_scan && pl.max_slots > 0) return run_seqsplit<Arm, DK, C, QF32>(pl, prm, parts, st);
+    if (parts > 0 && pl.run_prep && pl.run_scan && pl.max_slots > 0)
+      return run_seqsplit<Arm, DK, C, QF32, NCT>(pl, prm, parts, st);
   }
   if (pl.run_prep && !pl.fused && pl.max_slots > 0) {
     if constexpr (KDA) {
@@ -2143,8 +2272,8 @@ gdn_status run(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   if (pl.run_scan) {
-    const int64_t blocks = (int64_t)pl.n_seq * pl.hv * (pl.dv / 32);
-    if constexpr (!KDA && !QF32 && std::is_same<Arm, ArmBF16>::value) {
+    const int64_t blocks = prm.nscan;
+    if constexpr (!KDA && !QF32 && NCT == 1 && std::is_same<Arm, ArmBF16>::value) {
       if (pl.fused) {
         const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, true>::BYTES;
         if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, true>, lds)) return GDN_E_LAUNCH;
@@ -2153,12 +2282,20 @@ gdn_status run(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
       }
     }
     if (pl.fused) return GDN_E_UNSUPPORTED;  // refused on the host already
-    const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, false>::BYTES;
-    if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, false>, lds)) return GDN_E_LAUNCH;
-    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32, false>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
+    const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, false, NCT>::BYTES;
+    if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, false, NCT>, lds)) return GDN_E_LAUNCH;
+    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32, false, NCT>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
   return GDN_OK;
+}
+
+template <class Arm, int DK, int C, bool KDA, bool QF32>
+gdn_status run(const Plan& pl, const Params& prm, void* carry, hipStream_t st) {
+  if constexpr (std::is_same<Arm, ArmBF16>::value) {
+    if (scan_cols(pl) == 64) return run_cols<Arm, DK, C, KDA, QF32, 2>(pl, prm, carry, st);
+  }
+  return run_cols<Arm, DK, C, KDA, QF32, 1>(pl, prm, carry, st);
 }
 
 template <class Arm, int DK, bool QF32>
@@ -2190,7 +2327,7 @@ gdn_status run_arm(const Plan& pl, const Params& prm, void* carry, hipStream_t s
 
 int32_t plan_compose(const Plan& pl) {
   if (pl.fused) return GDN_COMPOSE_FUSED;
-  const int nscan = (int)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
+  const int nscan = (int)((int64_t)pl.n_seq * pl.hv * (pl.dv / scan_cols(pl)));
   if (!pl.gate_channel && pl.run_prep && pl.run_scan && pl.max_slots > 0 && pipelined_prep_wgs(pl, nscan) > 0)
     return GDN_COMPOSE_PIPELINED;
   if (!pl.gate_channel && pl.run_prep && pl.run_scan && pl.max_slots > 0 && seqsplit_parts(pl, nscan) > 0)

@@ -16,6 +16,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libgdn_mi355x.so")
+# the measurement build (built on request: python -m linear_attention_rnn_chunk_amd.build
+# --stamps), the same library plus per-phase timestamps of the scan
+STAMPS_LIBRARY_PATH = os.path.join(_HERE, "libgdn_mi355x_stamps.so")
 
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_ALIAS, GDN_E_WORKSPACE, GDN_E_LAUNCH = range(7)
 ST_NONFINITE_INPUT = 0x1
@@ -62,6 +65,17 @@ class GdnStatusError(RuntimeError):
 
 _lock = threading.Lock()
 _lib = None
+_path = LIBRARY_PATH
+
+
+def use_library(path: str) -> None:
+    """Load `path` (e.g. STAMPS_LIBRARY_PATH) instead of the product library; only before
+    the first call that loads one."""
+    global _path
+    with _lock:
+        if _lib is not None and path != _path:
+            raise RuntimeError("a library is already loaded: %s" % _path)
+        _path = path
 
 
 def load():
@@ -69,9 +83,9 @@ def load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIBRARY_PATH):
-                raise RuntimeError("libgdn_mi355x.so is not built (run __graft_entry__.build())")
-            lib = ctypes.CDLL(LIBRARY_PATH)
+            if not os.path.exists(_path):
+                raise RuntimeError("%s is not built (run __graft_entry__.build())" % os.path.basename(_path))
+            lib = ctypes.CDLL(_path)
             P = ctypes.POINTER(Problem)
             vp = ctypes.c_void_p
             lib.gdn_validate.argtypes = [P]
