@@ -14,7 +14,12 @@ Two independent evaluations live here:
   that builds every gate factor from pairwise exponent differences, following
   the same page's tile oracle (no midpoint factoring), with a LAPACK solve.
 
-Parity status: both pinned (tests/test_oracle_pins.py); they also pin each other.
+* :mod:`oracle.prepare` -- the input side next to the recurrence (raw q/k normalised per
+  row and scaled, beta = sigmoid(logit), g = -a softplus(x)), plainly in fp64, feeding
+  :func:`serial_fwd`.
+
+Parity status: all pinned (tests/test_oracle_pins.py, tests/test_oracle_prepare.py); the
+first two also pin each other.
 """
 from __future__ import annotations
 
