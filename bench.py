@@ -84,13 +84,15 @@ def scope_flops(spec, chunk):
 def composition_overhead_bytes(spec, chunk):
     """HBM bytes the split-type compositions move on top of the compulsory ones: every
     chunk's T and P fragments written by the prep and read back by the scan (per-channel
-    gate: also the gated operands e^G K, e^{G_C - G} K, e^G Q and the chunk decay)."""
+    gate: also the gated operands e^G K, e^{G_C - G} K, e^G Q and the chunk decay; raw
+    inputs: the two row-norm rows per chunk and key head)."""
     nch = sum((l + chunk - 1) // chunk for l in spec.seq_lens)
     tile = sum(mt // 2 + 1 for mt in range(chunk // 16)) * 512 * 2
     per = 2 * tile
     if spec.gate == "channel":
         per += 3 * chunk * spec.dk * 2 + spec.dk * 4
-    return 2 * nch * spec.hv * per
+    extra = 2 * nch * spec.hk * 2 * chunk * 4 if getattr(spec, "raw", False) else 0  # raw inputs: row norms
+    return 2 * nch * spec.hv * per + extra
 
 
 # the source file holding each workload's kernels and their launch code
@@ -783,12 +785,17 @@ def main():
     o = torch.empty((B, Tn, spec.hv, spec.dv), dtype=odt_t, device=dev)
     hT = torch.empty((spec.n_seq, spec.hv, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(1, gdn.workspace_bytes(p_all), gdn.workspace_bytes(p_prep)), dtype=torch.uint8,
-                     device=dev)
+    # raw-input workloads go through gdn_chunk_fwd_raw_inputs (same tensors, the raw values)
+    wsb = gdn.raw_workspace_bytes if spec.raw else gdn.workspace_bytes
+    ws = torch.empty(max(1, wsb(p_all), wsb(p_prep)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def call(prob):
-        rc = gdn.chunk_fwd_raw(prob, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
+        if spec.raw:
+            rc = gdn.chunk_fwd_raw_inputs_raw(prob, inp.meta["q_scale"], inp.meta["gate_scale"], q, k, v, g, beta, h0,
+                                              cu, o, hT, status, ws, stream.cuda_stream)
+        else:
+            rc = gdn.chunk_fwd_raw(prob, q, k, v, g, beta, h0, cu, o, hT, status, ws, stream.cuda_stream)
         if rc:
             raise gdn.GdnError(rc, "gdn_chunk_fwd")
 

@@ -178,6 +178,47 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_chunk_fwd_raw_inputs -- gdn_chunk_fwd from the raw per-token values next to the
+ * recurrence, which the generic operation takes prepared (the logismos issue #46 page,
+ * section "Remaining work": model-specific gating composed separately from the generic
+ * operation contract).  Each (token, head) row of q and k is divided by its L2 norm (a zero
+ * row stays zero) and q is then multiplied by q_scale; beta = sigmoid(logit); the
+ * natural-log decay is g = -gate_scale softplus(x) = -gate_scale log(1 + e^x).  These are
+ * the forms of the single-sequence, hybrid and packed workloads of the problem statement
+ * (q, k L2-normalised with q scaled by dk^-1/2, beta = sigmoid(N(0,1)), g = -a softplus(N(0,1))
+ * with a = 1/2 or 1).  Nothing is materialised: the prep kernel takes the row norms from the
+ * rows it loads anyway and folds them into its K K^T and Q K^T tiles, and the scan folds
+ * them into the per-row factors it already applies, so q and k are read as often as by
+ * gdn_chunk_fwd.
+ *   raw          q_scale > 0 and gate_scale > 0, both finite (else GDN_E_UNSUPPORTED); NULL is
+ *                refused with GDN_E_NULL
+ *   q_raw, k_raw [total_tokens][hk][dk] raw rows, qkv_dtype
+ *   gate_x       fp32 [total_tokens][hv] raw gate values (per-head gate only)
+ *   beta_logit   fp32 [total_tokens][hv]
+ *   workspace    at least gdn_raw_workspace_bytes() bytes (the row norms, 8 bytes per token
+ *                and key head, on top of gdn_workspace_bytes())
+ *   the rest     as for gdn_chunk_fwd
+ * Status bits: NONFINITE_INPUT for Inf/NaN in any raw value; GATE_DOMAIN cannot occur.
+ * Returns the codes of gdn_chunk_fwd; GDN_E_UNSUPPORTED also for the per-key-channel gate or
+ * the fused composition.
+ */
+typedef struct gdn_raw_inputs {
+  float q_scale;    /* q rows are multiplied by this after normalisation (e.g. dk^-1/2) */
+  float gate_scale; /* a in g = -a softplus(x) */
+} gdn_raw_inputs;
+
+/* gdn_raw_workspace_bytes -- bytes of workspace gdn_chunk_fwd_raw_inputs needs for *p
+ * (written to *bytes): gdn_workspace_bytes plus the row norms.  Host-only; the codes of
+ * gdn_workspace_bytes, and GDN_E_UNSUPPORTED where raw inputs are not supported. */
+gdn_status gdn_raw_workspace_bytes(const gdn_problem* p, size_t* bytes);
+
+gdn_status gdn_chunk_fwd_raw_inputs(const gdn_problem* p, const gdn_raw_inputs* raw, const void* q_raw,
+                                    const void* k_raw, const void* v, const float* gate_x,
+                                    const float* beta_logit, const float* h0, const int32_t* cu_seqlens,
+                                    void* o, float* hT, uint32_t* status, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * The same computation, kernels and launches as gdn_chunk_fwd with the composition

@@ -18,7 +18,7 @@ static int32_t g_stamp_block = 0, g_stamp_c0 = 0;
 
 static inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-gdn_status make_plan(const gdn_problem* p, Plan* out) {
+gdn_status make_plan(const gdn_problem* p, Plan* out, bool raw) {
   if (!p || !out) return GDN_E_NULL;
   if (p->n_seq < 0 || p->total_tokens < 0 || p->seq_len < 0 || p->hk < 1 || p->hv < 1)
     return GDN_E_SHAPE;
@@ -55,8 +55,12 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   // additionally needs square states: a transition is a dk x dk state scanned like a value
   const bool seq_ok = pipe_ok && p->dk == p->dv;
   if (p->compose == GDN_COMPOSE_SEQSPLIT && !seq_ok) return GDN_E_UNSUPPORTED;
+  // raw inputs: the per-head gate, split or pipelined (the row norms pass through the
+  // workspace from the prep to the scan; the fused composition has no such stage)
+  if (raw && (p->gate != GDN_GATE_HEAD || p->compose == GDN_COMPOSE_FUSED)) return GDN_E_UNSUPPORTED;
   Plan pl;
   memset(&pl, 0, sizeof(pl));
+  pl.raw = raw;
   pl.n_seq = p->n_seq;
   pl.seq_len = p->seq_len;
   pl.hk = p->hk;
@@ -135,6 +139,10 @@ gdn_status make_plan(const gdn_problem* p, Plan* out) {
   const size_t parts = pl.seq_ok ? 3 * (size_t)kMaxParts * pl.n_seq * pl.hv * pl.dk * pl.dv * 4 : 0;
   pl.off_parts = off;
   off = round_up(off + parts, 256);
+  // raw inputs: 1 / |k| and q_scale / |q| of every row, per tile slot and key head
+  const size_t norms = raw ? (size_t)pl.tile_slots * pl.hk * 2 * C * 4 : 0;
+  pl.off_N = off;
+  off = round_up(off + norms, 256);
   pl.bytes = off;
   *out = pl;
   return GDN_OK;
@@ -174,13 +182,20 @@ gdn_status gdn_workspace_bytes(const gdn_problem* p, size_t* bytes) {
   return GDN_OK;
 }
 
-gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, const float* h0,
-                         const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace gdn {
+
+// gdn_chunk_fwd, and with `raw` gdn_chunk_fwd_raw_inputs
+static gdn_status chunk_fwd(const gdn_problem* p, const gdn_raw_inputs* raw, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta, const float* h0,
+                            const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   gdn::Plan pl;
-  gdn_status s = gdn::make_plan(p, &pl);
+  gdn_status s = gdn::make_plan(p, &pl, raw != nullptr);
   if (s != GDN_OK) return s;
+  if (raw && !(raw->q_scale > 0.f && raw->gate_scale > 0.f && raw->q_scale < 3.4e38f && raw->gate_scale < 3.4e38f))
+    return GDN_E_UNSUPPORTED;  // positive and finite
   if (!status) return GDN_E_NULL;
   if (pl.total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_E_NULL;
   if (p->seq_len > 0 && cu_seqlens) return GDN_E_SHAPE;  // one description of the sequences
@@ -252,6 +267,12 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
   prm.prep_ce = prm.seg_ce;
   prm.nscan = (int32_t)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
   prm.h0_input = 1;
+  if (raw) {
+    prm.raw = 1;
+    prm.q_scale = raw->q_scale;
+    prm.gate_scale = raw->gate_scale;
+    prm.Nws = (float*)(ws + pl.off_N);
+  }
 #ifdef GDN_SCAN_STAMPS
   prm.stamps = gdn::g_stamps;
   prm.stamp_block = gdn::g_stamp_block;
@@ -264,6 +285,37 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
     prm.Hws = prm.Mws + one;
   }
   return gdn::launch(pl, prm, ws ? ws + pl.off_carry : nullptr, stream);
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* h0,
+                         const int32_t* cu_seqlens, void* o, float* hT, uint32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return gdn::chunk_fwd(p, nullptr, q, k, v, g, beta, h0, cu_seqlens, o, hT, status, workspace,
+                        workspace_bytes, stream);
+}
+
+gdn_status gdn_raw_workspace_bytes(const gdn_problem* p, size_t* bytes) {
+  if (!bytes) return GDN_E_NULL;
+  gdn::Plan pl;
+  gdn_status s = gdn::make_plan(p, &pl, true);
+  if (s != GDN_OK) return s;
+  *bytes = pl.bytes;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_raw_inputs(const gdn_problem* p, const gdn_raw_inputs* raw, const void* q_raw,
+                                    const void* k_raw, const void* v, const float* gate_x,
+                                    const float* beta_logit, const float* h0, const int32_t* cu_seqlens,
+                                    void* o, float* hT, uint32_t* status, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!raw) return GDN_E_NULL;
+  return gdn::chunk_fwd(p, raw, q_raw, k_raw, v, gate_x, beta_logit, h0, cu_seqlens, o, hT, status, workspace,
+                        workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,

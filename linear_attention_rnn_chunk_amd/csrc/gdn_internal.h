@@ -51,9 +51,10 @@ struct Plan {
   int32_t tile_ring;     // chunks per ring half of the tile buffers (pipelined composition on
                          // sequences longer than two segments), else 0: every chunk its own slot
   int64_t tile_slots;    // chunk slots the tile buffers hold
+  int32_t raw;           // 1: raw inputs (gdn_chunk_fwd_raw_inputs)
   // workspace carve-up (byte offsets)
   int32_t kq_ws;         // 1: K and Q copied to the workspace in the arm's type
-  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, off_carry, off_parts, bytes;
+  size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, off_carry, off_parts, off_N, bytes;
 };
 
 // Kernel arguments (by value).
@@ -107,6 +108,12 @@ struct Params {
   // [kStampSteps steps from chunk stamp_c0][kStampPhases] shader-clock counts.
   uint64_t* stamps;
   int32_t stamp_block, stamp_c0;
+  // Raw inputs: q, k are raw rows (normalised per (token, head) inside, q then scaled by
+  // q_scale), beta holds logits (beta = sigmoid), g raw values (g = -gate_scale softplus).
+  // Nws: [tile slot][hk][2][C] fp32, 1 / |k_r| then q_scale / |q_r|, from the prep.
+  int32_t raw;
+  float q_scale, gate_scale;
+  float* Nws;
 };
 constexpr int kStampSteps = 16, kStampPhases = 8;
 
@@ -125,7 +132,7 @@ struct DecodeParams {
   int32_t qkv_f32, o_f32;
 };
 
-gdn_status make_plan(const gdn_problem* p, Plan* plan);
+gdn_status make_plan(const gdn_problem* p, Plan* plan, bool raw = false);
 gdn_status launch_decode(const DecodeParams& prm, int dk, bool per_channel_gate, void* stream);
 gdn_status launch(const Plan& plan, const Params& prm, void* carry, void* stream);
 // the composition launch() runs for this plan on the current device (GDN_COMPOSE_*)

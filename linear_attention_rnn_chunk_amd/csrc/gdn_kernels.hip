@@ -62,6 +62,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 // e^x through the hardware exp2 (v_exp_f32); e^-inf = 0, large negative x flush to 0.
 __device__ __forceinline__ float nexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// The input side from raw per-token values (the gdn_chunk_fwd_raw_inputs entry point):
+// beta = sigmoid(logit) and g = -a softplus(x) = -a (max(x, 0) + log(1 + e^-|x|)), through
+// the hardware exp2 / log2 (v_exp_f32, v_log_f32) with no overflow for any finite input.
+constexpr float kLn2 = 0.69314718055994531f;
+__device__ __forceinline__ float sigmoid_f(float x) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);  // e^-|x|, in (0, 1]
+  const float r = 1.f / (1.f + e);
+  return x >= 0.f ? r : e * r;
+}
+__device__ __forceinline__ float neg_softplus(float x, float a) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  return -a * (fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 // Inf/NaN tests as bit arithmetic: no short-circuit branches, so loads around them
@@ -443,7 +457,9 @@ __host__ __device__ constexpr int tri(int rt, int st) { return rt * (rt + 1) / 2
 template <int C>
 struct SolveLds {
   static constexpr int NT = C / 16, NTRI = NT * (NT + 1) / 2;
-  static constexpr int FLOATS = NTRI * kTile + 2 * C;
+  // the lower tiles, then the chunk's G and beta rows and (raw inputs) 1 / |k_r| and
+  // q_scale / |q_r|
+  static constexpr int FLOATS = NTRI * kTile + 4 * C;
 };
 
 // One wave's LDS accesses in program order, complete: data some lanes wrote is then
@@ -525,32 +541,38 @@ __device__ __forceinline__ void wave_solve_unit_lower(float* S, int lane) {
 //   A = tril_strict(beta_r e^{G_r - G_s} KK),  P = tril(e^{G_r - G_s} QK), rows r < L
 // (per-channel gate: the exponentials are already inside the products, G unused);
 // then T = (I + A)^-1 in this wave's LDS S, and T, P stored as scan fragments.
+// Raw inputs (Nk, Nq non-null: 1 / |k_r| and q_scale / |q_r| of the chunk's rows in LDS):
+// the products of the raw rows become those of the normalised rows, A_rs by Nk_r Nk_s and
+// P_rs by Nq_r Nk_s (without them every factor is exactly 1, so the bits are unchanged).
 template <class Arm, int C, bool KDA>
 __device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, const float* Gs,
                                            const float* Bs, typename Arm::T* Tout,
-                                           typename Arm::T* Pout, int L, int lane) {
+                                           typename Arm::T* Pout, int L, int lane,
+                                           const float* Nk = nullptr, const float* Nq = nullptr) {
   constexpr int NT = C / 16;
   const int i = lane & 15, g = lane >> 4;
-  wave_lds_sync();  // G and beta rows written by other lanes
+  wave_lds_sync();  // G and beta rows (and row norms) written by other lanes
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     const float Gr = KDA ? 0.f : Gs[16 * rt + i];
-    const float br = Bs[16 * rt + i];  // zero for rows past the chunk end
+    const float nkr = Nk ? Nk[16 * rt + i] : 1.f, nqr = Nk ? Nq[16 * rt + i] : 1.f;
+    const float br = Bs[16 * rt + i] * nkr;  // zero for rows past the chunk end
     const bool live = 16 * rt + i < L;
 #pragma unroll
     for (int st = 0; st <= rt; ++st) {
       const int t = tri(rt, st);
-      float4 G4 = {0.f, 0.f, 0.f, 0.f};
+      float4 G4 = {0.f, 0.f, 0.f, 0.f}, N4 = {1.f, 1.f, 1.f, 1.f};
       if constexpr (!KDA) G4 = *(const float4*)(Gs + 16 * st + 4 * g);
-      const float Gsv[4] = {G4.x, G4.y, G4.z, G4.w};
+      if (Nk) N4 = *(const float4*)(Nk + 16 * st + 4 * g);
+      const float Gsv[4] = {G4.x, G4.y, G4.z, G4.w}, Nks[4] = {N4.x, N4.y, N4.z, N4.w};
       f32x4 a, pv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool lower = st < rt || 4 * g + j < i;
         const bool ldiag = live && (st < rt || 4 * g + j <= i);
-        const float e = KDA ? 1.f : nexp(Gr - Gsv[j]);  // s > r entries are discarded
+        const float e = (KDA ? 1.f : nexp(Gr - Gsv[j])) * Nks[j];  // s > r entries are discarded
         a[j] = lower ? br * (e * accA[t][j]) : 0.f;
-        pv[j] = ldiag ? e * accP[t][j] : 0.f;
+        pv[j] = ldiag ? (e * accP[t][j]) * nqr : 0.f;
       }
       *(float4*)(S + t * kTile + i * kTP + 4 * g) = (float4){a[0], a[1], a[2], a[3]};
       accP[t] = pv;
@@ -733,10 +755,16 @@ __device__ __forceinline__ uint32_t tile_products_lean(const Params& p, int64_t 
 
 // G (inclusive prefix of the gate) and beta of the chunk's rows into Gs, Bs (rows past
 // the end contribute gate 0 and beta 0); returns the status bits of the gate and beta
+// (raw inputs: xl and bl are the raw gate value and the beta logit, transformed here)
 template <int C>
-__device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int lane, float* Gs, float* Bs) {
-  const float x = lane < L ? xl : 0.f, b = lane < L ? bl : 0.f;
+__device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int lane, float* Gs, float* Bs,
+                                               const Params& p) {
+  float x = lane < L ? xl : 0.f, b = lane < L ? bl : 0.f;
   uint32_t bad = flag_if(f_nonfinite(x) | f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
+  if (p.raw && lane < L) {
+    x = neg_softplus(x, p.gate_scale);
+    b = sigmoid_f(b);
+  }
   bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
   const float G = wave_prefix_sum(x, lane);
   if (lane < C) {
@@ -744,6 +772,52 @@ __device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int la
     Bs[lane] = b;
   }
   return bad;
+}
+
+// Raw inputs: 1 / |k_r| and q_scale / |q_r| of the chunk's rows (0 for a zero row; rows past
+// the chunk end repeat the last row) from the loaded K and Q fragments -- lane (i, g) holds 8
+// elements of row 16 rt + i per key block, the four lanes i + 16 g together the whole row --
+// into Nk, Nq (LDS) and, when `out` is set, to out[0 .. C) and out[C .. 2C) (workspace).
+template <int DK, int C, bool QF32>
+__device__ __forceinline__ void tile_row_norms(const TileRegs<DK, C, QF32>& R, float qs, int lane, float* Nk,
+                                               float* Nq, float* out) {
+  constexpr int NT = C / 16, NBK = DK / 32, EPL = QF32 ? 2 : 1;
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb)
+#pragma unroll
+      for (int x = 0; x < EPL; ++x)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t uk = R.rk[kb][rt][x][w], uq = R.rq[kb][rt][x][w];
+          if constexpr (QF32) {
+            const float a = __uint_as_float(uk), b = __uint_as_float(uq);
+            sk = fmaf(a, a, sk);
+            sq = fmaf(b, b, sq);
+          } else {
+            const float a0 = __uint_as_float(uk << 16), a1 = __uint_as_float(uk & 0xFFFF0000u);
+            const float b0 = __uint_as_float(uq << 16), b1 = __uint_as_float(uq & 0xFFFF0000u);
+            sk = fmaf(a1, a1, fmaf(a0, a0, sk));
+            sq = fmaf(b1, b1, fmaf(b0, b0, sq));
+          }
+        }
+    sk += __shfl_xor(sk, 16, 64);
+    sq += __shfl_xor(sq, 16, 64);
+    sk += __shfl_xor(sk, 32, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    if (g == 0) {
+      const float nk = sk > 0.f ? 1.f / __builtin_sqrtf(sk) : 0.f, nq = sq > 0.f ? qs / __builtin_sqrtf(sq) : 0.f;
+      Nk[16 * rt + i] = nk;
+      Nq[16 * rt + i] = nq;
+      if (out) {
+        out[16 * rt + i] = nk;
+        out[C + 16 * rt + i] = nq;
+      }
+    }
+  }
 }
 
 // One (chunk slot, value head) unit of the per-head-gate prep on one wave, in two
@@ -779,7 +853,12 @@ __device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, 
   const int64_t slot = store_slot(p, U.slot);
   float* Gs = S + NTRI * kTile;
   float* Bs = Gs + C;
-  uint32_t bad = tile_sweep<C>(U.R.xl, U.R.bl, L, lane, Gs, Bs);
+  float* Nk = p.raw ? Bs + C : nullptr;
+  float* Nq = Bs + 2 * C;
+  uint32_t bad = tile_sweep<C>(U.R.xl, U.R.bl, L, lane, Gs, Bs, p);
+  if (p.raw)  // (the group's first value head also stores them for the scan)
+    tile_row_norms<DK, C, QF32>(U.R, p.q_scale, lane, Nk, Nq,
+                                j == 0 ? p.Nws + (slot * p.hk + kh) * (int64_t)(2 * C) : nullptr);
   if (j == 0) {  // once per key head (wave-uniform)
     bad |= tile_kq_nonfinite<DK, C, QF32>(U.R);
     if (p.kq_ws) {
@@ -802,7 +881,7 @@ __device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, 
   tile_products<Arm, DK, C, QF32>(U.R, accA, accP);
   typedef typename Arm::T T;
   const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
-  wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
+  wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, Nk, Nq);
   if (bad) atomicOr(p.status, bad);
 }
 
@@ -894,6 +973,10 @@ __device__ __forceinline__ void prep_role(const Params& p) {
         bs[j] = p.beta[(t0 + rg) * p.hv + h0 + j];
       }
     uint32_t bad = tile_kq_nonfinite<DK, C, QF32>(R);
+    float* Nk = p.raw ? Bs + C : nullptr;
+    float* Nq = Bs + 2 * C;
+    if (p.raw)  // row norms once per key head, for every value head of the group and the scan
+      tile_row_norms<DK, C, QF32>(R, p.q_scale, lane, Nk, Nq, p.Nws + (slot * p.hk + kh) * (int64_t)(2 * C));
     if (p.kq_ws) {  // K and Q in the arm's element type (as in prep_finish)
       T* kc = (T*)p.Kws + (slot * p.hk + kh) * (int64_t)(C * DK);
       T* qc = (T*)p.Qws + (slot * p.hk + kh) * (int64_t)(C * DK);
@@ -923,7 +1006,7 @@ __device__ __forceinline__ void prep_role(const Params& p) {
         xl = p.g[(t0 + rg) * p.hv + h0 + j];
         bl = p.beta[(t0 + rg) * p.hv + h0 + j];
       }
-      bad |= tile_sweep<C>(xl, bl, L, lane, Gs, Bs);
+      bad |= tile_sweep<C>(xl, bl, L, lane, Gs, Bs, p);
       f32x4 accA[NTRI], accP[NTRI];
 #pragma unroll
       for (int t = 0; t < NTRI; ++t) {
@@ -931,7 +1014,7 @@ __device__ __forceinline__ void prep_role(const Params& p) {
         accP[t] = P0[t];
       }
       const int64_t tofs = (slot * p.hv + h0 + j) * (int64_t)tile_elems(C);
-      wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
+      wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, Nk, Nq);
     }
     if (bad) atomicOr(p.status, bad);
   }
@@ -1232,8 +1315,9 @@ struct ScanLds {
   //       slots, all after the exchange
   // (Measured for the split scan at dk = 128, C = 64: the slot layout with the copy wave
   // moving T and P is 1.5 % slower; giving up Q in the ring for a fourth buffer, 17 %.)
+  static constexpr int NRB = KDA ? 0 : 2 * C * 4;  // raw inputs: 1 / |k_r| and q_scale / |q_r| rows
   static constexpr int base_bytes(bool qr) {
-    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * WC * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256;
+    return (KDA ? 2 : 1) * OPB + (qr ? OPB : 0) + rnd(C * WC * ESZV) + (KDA ? 0 : 256) + 256 + NDD * 256 + NRB;
   }
   static constexpr int FIXA = EXCH + 4 * TILEB + SSB;
   static constexpr bool QRA = 2 * base_bytes(true) + FIXA + 2 * SCB <= LDS_MAX;
@@ -1268,7 +1352,8 @@ struct ScanLds {
   static constexpr int GX = VV + rnd(C * WC * ESZV);  // gate rows (per-head gate)
   static constexpr int GB = GX + (KDA ? 0 : 256);     // beta rows
   static constexpr int DC = GB + 256;                 // e^{G_C} per key channel
-  static constexpr int SC = DC + NDD * 256;           // !TL: row scalars
+  static constexpr int NR = DC + NDD * 256;           // raw inputs: the chunk's row norms
+  static constexpr int SC = NR + NRB;                 // !TL: row scalars
   static constexpr int BUF = SC + (TL ? 0 : SCB);
   static_assert(BUF == (TL ? BUFA : BUFB), "buffer carve-up");
   // after the exchange (TL): T slots, P slots, scalar slots, then the fused solve scratch
@@ -1498,6 +1583,12 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         const float* D = p.Dws + ((slot0 + ci) * hvs + h) * (int64_t)DK;
 #pragma unroll
         for (int m = 0; m < SL::NDD; ++m) dma4(D + min(lane + 64 * m, DK - 1), B + SL::DC + m * 256);
+      } else {
+        if (p.raw) {  // the chunk's row norms, as the prep stored them (two more copies)
+          const float* N = p.Nws + ((slot0 + ci) * p.hk + kh) * (int64_t)(2 * C) + (lane < C ? lane : C - 1);
+          dma4(N, B + SL::NR);
+          dma4(N + C, B + SL::NR + 4 * C);
+        }
       }
     };
     auto sweep = [&](int ci) __attribute__((always_inline)) {  // scalars of chunk ci
@@ -1505,21 +1596,32 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       float* S = scal(ci);
       const int L = chunk_L(ci);
       const float bl = ((const float*)(B + SL::GB))[lane];
-      const float b = lane < L ? bl : 0.f;
+      float b = lane < L ? bl : 0.f;
       bad |= flag_if(f_nonfinite(b), GDN_ST_NONFINITE_INPUT);
       if constexpr (!KDA) {
         const float xl = ((const float*)(B + SL::GX))[lane];
-        const float x = lane < L ? xl : 0.f;
+        float x = lane < L ? xl : 0.f;
         bad |= flag_if(f_nonfinite(x), GDN_ST_NONFINITE_INPUT);
+        // raw inputs: beta and the gate from the logit and the raw value, the row norms of
+        // k (in Y = K H and the state update) and of q (with its scale) for the scalars
+        float nk = 1.f, nq = 1.f;
+        if (p.raw) {
+          if (lane < L) {
+            x = neg_softplus(x, p.gate_scale);
+            b = sigmoid_f(b);
+          }
+          nk = ((const float*)(B + SL::NR))[lane < C ? lane : C - 1];
+          nq = ((const float*)(B + SL::NR + 4 * C))[lane < C ? lane : C - 1];
+        }
         bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
         const float G = wave_prefix_sum_dpp(x);
         const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
         if (lane < C) {
           const float eg = nexp(G);
           S[lane] = b;
-          S[C + lane] = b * eg;
-          S[2 * C + lane] = nexp(GC - G);
-          S[3 * C + lane] = eg;
+          S[C + lane] = b * eg * nk;
+          S[2 * C + lane] = nexp(GC - G) * nk;
+          S[3 * C + lane] = eg * nq;
         }
         if (lane == 0) S[4 * C] = nexp(GC);
       } else {
@@ -1540,11 +1642,17 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // one chunk's copies (LA - CL <= 1) may stay in flight past a wait, so each wait
     // allows either ND outstanding copies (when a later chunk was issued) or none.
     static_assert(LA - CL <= 1, "one chunk in flight beyond the completed window");
+    // (raw inputs: two more copies per chunk, the row norms)
+    const bool xr = !KDA && p.raw;
 #pragma unroll
     for (int j = 0; j < LA; ++j)
       if (j < nch) issue(j);
-    if (LA > CL && nch > LA - 1) wait_vm<(LA > CL ? SL::ND : 0)>();
-    else wait_vm<0>();
+    if (LA > CL && nch > LA - 1) {
+      if (xr) wait_vm<(LA > CL ? SL::ND + 2 : 0)>();
+      else wait_vm<(LA > CL ? SL::ND : 0)>();
+    } else {
+      wait_vm<0>();
+    }
 #pragma unroll
     for (int j = 0; j < CL; ++j)
       if (j < nch) sweep(j);
@@ -1556,8 +1664,12 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       GDN_STAMP(2, ci, 1);
       // chunk ci + CL complete: all copies but this step's, which stay in flight across
       // the barrier
-      if (LA > CL && more) wait_vm<(LA > CL ? SL::ND : 0)>();
-      else wait_vm<0>();
+      if (LA > CL && more) {
+        if (xr) wait_vm<(LA > CL ? SL::ND + 2 : 0)>();
+        else wait_vm<(LA > CL ? SL::ND : 0)>();
+      } else {
+        wait_vm<0>();
+      }
       GDN_STAMP(2, ci, 2);
       if (ci + CL < nch) sweep(ci + CL);
       check_v(ci);
@@ -2032,7 +2144,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int L = chunk_L(cu);
-      bad |= tile_sweep<C>(xl, bl, L, ln, Gs, Bs);
+      bad |= tile_sweep<C>(xl, bl, L, ln, Gs, Bs, p);
       T* Tout = (T*)(exch + SL::TT + (cu & 1) * SL::TILEB);
       T* Pout = (T*)(exch + SL::TP + (cu & 1) * SL::TILEB);
       wave_tiles<Arm, C, false>(accA, accP, Sv, Gs, Bs, Tout, Pout, L, ln);

@@ -33,7 +33,8 @@ STAGE_ALL, STAGE_PREP, STAGE_SCAN = 0, 1, 2
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_plan_compose", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc",
-           "gdn_decode_step", "gdn_error_string", "gdn_status_string", "gdn_abi_version")
+           "gdn_raw_workspace_bytes", "gdn_chunk_fwd_raw_inputs", "gdn_decode_step", "gdn_error_string",
+           "gdn_status_string", "gdn_abi_version")
 # the largest workspace gdn_chunk_fwd_noalloc serves (its per-device array)
 NOALLOC_WORKSPACE_BYTES = 64 << 20
 
@@ -45,6 +46,11 @@ class Problem(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("arm", ctypes.c_int32), ("compose", ctypes.c_int32),
                 ("stages", ctypes.c_int32)]
+
+
+class RawInputs(ctypes.Structure):
+    """gdn_raw_inputs: q rows scaled by q_scale after normalisation; g = -gate_scale softplus(x)."""
+    _fields_ = [("q_scale", ctypes.c_float), ("gate_scale", ctypes.c_float)]
 
 
 class GdnError(RuntimeError):
@@ -99,6 +105,11 @@ def load():
             lib.gdn_chunk_fwd.restype = ctypes.c_int
             lib.gdn_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+            lib.gdn_raw_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn_raw_workspace_bytes.restype = ctypes.c_int
+            lib.gdn_chunk_fwd_raw_inputs.argtypes = [P, ctypes.POINTER(RawInputs), vp, vp, vp, vp, vp, vp, vp, vp,
+                                                     vp, vp, vp, ctypes.c_size_t, vp]
+            lib.gdn_chunk_fwd_raw_inputs.restype = ctypes.c_int
             lib.gdn_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.gdn_decode_step.restype = ctypes.c_int
             lib.gdn_error_string.argtypes = [ctypes.c_int32]
@@ -142,6 +153,15 @@ def workspace_bytes(prob: Problem) -> int:
     return int(n.value)
 
 
+def raw_workspace_bytes(prob: Problem) -> int:
+    """Workspace bytes of gdn_chunk_fwd_raw_inputs for `prob`."""
+    n = ctypes.c_size_t(0)
+    rc = load().gdn_raw_workspace_bytes(ctypes.byref(prob), ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_raw_workspace_bytes")
+    return int(n.value)
+
+
 def plan_compose(prob: Problem) -> int:
     """The composition gdn_chunk_fwd runs for `prob` on the current device (COMPOSE_*)."""
     c = ctypes.c_int32(-1)
@@ -173,6 +193,19 @@ def chunk_fwd_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT, status
         ctypes.c_void_p(int(stream))))
 
 
+def chunk_fwd_raw_inputs_raw(prob: Problem, q_scale, gate_scale, q, k, v, gate_x, beta_logit, h0, cu_seqlens, o, hT,
+                             status, workspace, stream=None) -> int:
+    """Direct call of gdn_chunk_fwd_raw_inputs with caller-owned tensors; returns the host code."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    raw = RawInputs(float(q_scale), float(gate_scale))
+    return int(load().gdn_chunk_fwd_raw_inputs(
+        ctypes.byref(prob), ctypes.byref(raw), _ptr(q), _ptr(k), _ptr(v), _ptr(gate_x), _ptr(beta_logit), _ptr(h0),
+        _ptr(cu_seqlens), _ptr(o), _ptr(hT), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+        ctypes.c_void_p(int(stream))))
+
+
 def chunk_fwd_noalloc_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT, status,
                           stream=None) -> int:
     """Direct call of gdn_chunk_fwd_noalloc (the library's own per-device workspace, no
@@ -186,8 +219,12 @@ def chunk_fwd_noalloc_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT
 
 def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm: str = "bf16",
               o_dtype: Optional[torch.dtype] = None, compose: str = "auto", want_hT: bool = True,
-              check: bool = True, workspace: Optional[torch.Tensor] = None):
+              check: bool = True, workspace: Optional[torch.Tensor] = None, raw: Optional[tuple] = None):
     """Chunkwise gated delta-rule prefill on the current device and stream.
+
+    With ``raw = (q_scale, gate_scale)`` the inputs are the raw per-token values
+    (gdn_chunk_fwd_raw_inputs): q, k raw rows (normalised inside, q then scaled), beta the
+    logits (beta = sigmoid), g the raw gate values (g = -gate_scale softplus), per-head gate.
 
     Fixed-length batch: q, k [B, T, HK, DK]; v [B, T, HV, DV]; g [B, T, HV] (per-head
     gate) or [B, T, HV, DK] (per-key-channel gate); beta [B, T, HV]; h0 [B, HV, DK, DV].
@@ -234,16 +271,22 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm
     rc = validate(prob)
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_validate")
+    if raw is not None and gate != GATE_HEAD:
+        raise GdnError(GDN_E_UNSUPPORTED, "raw inputs: per-head gate only")
     dev = q.device
     o = torch.empty((B, T, HV, DV), dtype=odt, device=dev)
     hT = torch.empty((n_seq, HV, DK, DV), dtype=torch.float32, device=dev) if want_hT else None
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    need = workspace_bytes(prob)
+    need = raw_workspace_bytes(prob) if raw is not None else workspace_bytes(prob)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    rc = chunk_fwd_raw(prob, q, k, v, g, beta, h0, cu_seqlens, o, hT, status, workspace)
+    if raw is not None:
+        rc = chunk_fwd_raw_inputs_raw(prob, raw[0], raw[1], q, k, v, g, beta, h0, cu_seqlens, o, hT, status,
+                                      workspace)
+    else:
+        rc = chunk_fwd_raw(prob, q, k, v, g, beta, h0, cu_seqlens, o, hT, status, workspace)
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_chunk_fwd")
+        raise GdnError(rc, "gdn_chunk_fwd_raw_inputs" if raw is not None else "gdn_chunk_fwd")
     if check:
         torch.cuda.current_stream().synchronize()
         bits = int(status.item()) & 0xFFFFFFFF

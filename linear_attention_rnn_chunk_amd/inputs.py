@@ -57,6 +57,8 @@ class Spec:
     seed: int = 0
     beta_law: str = "sigmoid"      # sigmoid | one | zero | eps
     qk_same: bool = False          # q is a copy of k (after k's normalisation and cast)
+    raw: bool = False              # keep the raw draws: q, k unnormalised (and q unscaled),
+                                   # beta = the logits, g = the raw gate values (laws half, full)
 
     @property
     def tokens(self) -> int:
@@ -80,6 +82,10 @@ CONFIGS = {
                 chunk=32, seed=1004),
     "packed": Spec("packed", (65536, 32768, 24576, 8192), 16, 48, 128, 128, gate_law="full",
                    h0=True, chunk=64, packed=True, seed=1005),
+    # the hybrid layer's draws before their preparation: raw q, k, beta logits, raw gate
+    # values (for the raw-input entry point: q_scale 128^-1/2, gate_scale 1/2)
+    "hybrid_raw": Spec("hybrid_raw", (32768,), 16, 48, 128, 128, gate_law="half", h0=True, chunk=64,
+                       seed=1003, raw=True),
 }
 
 
@@ -147,13 +153,22 @@ def make(spec, seed: Optional[int] = None) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(spec.seed))
     tok, hk, hv, dk, dv = spec.tokens, spec.hk, spec.hv, spec.dk, spec.dv
 
-    q = _l2norm_rows(_normal(rng, (tok, hk, dk)))
-    if spec.q_scale:
+    qd, kd = _normal(rng, (tok, hk, dk)), None
+    q = qd if spec.raw else _l2norm_rows(qd)
+    if spec.q_scale and not spec.raw:
         q *= np.float32(dk ** -0.5)
-    k = _l2norm_rows(_normal(rng, (tok, hk, dk)))
+    kd = _normal(rng, (tok, hk, dk))
+    k = kd if spec.raw else _l2norm_rows(kd)
     v = _normal(rng, (tok, hv, dv))
     blog = _normal(rng, (tok, hv))
-    if spec.beta_law == "sigmoid":
+    meta = {}
+    if spec.raw:
+        if spec.beta_law != "sigmoid" or spec.gate != "head" or spec.gate_law not in ("half", "full"):
+            raise ValueError("raw draws: sigmoid beta law, per-head gate, gate law half or full")
+        meta = dict(q_scale=float(np.float32(dk ** -0.5)) if spec.q_scale else 1.0,
+                    gate_scale=0.5 if spec.gate_law == "half" else 1.0)
+        beta = blog
+    elif spec.beta_law == "sigmoid":
         beta = (1.0 / (1.0 + np.exp(-blog.astype(np.float64)))).astype(np.float32)
     elif spec.beta_law == "one":
         beta = np.ones((tok, hv), np.float32)
@@ -172,7 +187,9 @@ def make(spec, seed: Optional[int] = None) -> Inputs:
         g = rng.uniform(-0.5, 0.0, size=gshape).astype(np.float32)
     else:
         graw = _normal(rng, gshape)
-        if law == "clip5":
+        if spec.raw:
+            g = graw
+        elif law == "clip5":
             g = np.clip(-_softplus(graw), -5.0, 0.0).astype(np.float32)
         elif law == "half":
             g = (-0.5 * _softplus(graw)).astype(np.float32)
@@ -193,4 +210,4 @@ def make(spec, seed: Optional[int] = None) -> Inputs:
         raise ValueError(spec.qkv_dtype)
     cu = np.zeros(spec.n_seq + 1, dtype=np.int32)
     cu[1:] = np.cumsum(np.asarray(spec.seq_lens, dtype=np.int64))
-    return Inputs(spec, q, k, v, g, beta, h0, cu)
+    return Inputs(spec, q, k, v, g, beta, h0, cu, meta)

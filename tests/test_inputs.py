@@ -42,3 +42,16 @@ def test_small_bf16_spec_rounds_and_scales_q():
     assert np.allclose(qn, 128 ** -0.5, rtol=1e-2)
     assert a.h0 is None
     assert a.g.shape == (70, 6)
+
+
+def test_raw_draws_are_the_prepared_workloads_draws_before_preparation():
+    spec = inputs.CONFIGS["hybrid"].with_(seq_lens=(70,), hk=2, hv=6, qkv_dtype="f32")
+    a, r = inputs.make(spec), inputs.make(spec.with_(raw=True))
+    assert r.meta == dict(q_scale=float(np.float32(128 ** -0.5)), gate_scale=0.5)
+    assert np.array_equal(inputs._l2norm_rows(r.k), a.k)
+    assert np.array_equal(inputs._l2norm_rows(r.q) * np.float32(128 ** -0.5), a.q)
+    assert np.allclose(1.0 / (1.0 + np.exp(-r.beta.astype(np.float64))), a.beta, rtol=1e-6)
+    assert np.allclose(-0.5 * np.logaddexp(0.0, r.g.astype(np.float64)), a.g, rtol=1e-6)
+    assert np.array_equal(r.v, a.v) and np.array_equal(r.h0, a.h0)
+    with pytest.raises(ValueError):
+        inputs.make(inputs.CONFIGS["tiny"].with_(raw=True))   # clip5 gate law: no raw form
