@@ -633,7 +633,8 @@ def layer_problem(args, spec, compose, stages=0):
     odt = gdn.BF16 if args.arm == "bf16" else gdn.F32
     arm = gdn.ARM_MFMA_BF16 if args.arm == "bf16" else gdn.ARM_FOLD_F32
     return gdn.make_problem(spec.n_seq, spec.tokens, 0 if packed else spec.seq_lens[0], spec.hk, spec.hv,
-                            spec.dk, spec.dv, gate, chunk, qdt, odt, arm, compose, stages)
+                            spec.dk, spec.dv, gate, chunk, qdt, odt, arm, compose, stages,
+                            solve_block=getattr(args, "solve_block", 0))
 
 
 COMPOSE_NAMES = ("auto", "split", "fused", "pipelined", "seqsplit")
@@ -654,6 +655,8 @@ def main():
     ap.add_argument("--config", default="hybrid")
     ap.add_argument("--arm", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--solve-block", type=int, default=0, choices=[0, 8, 16, 32],
+                    help="rows of the triangular solve's diagonal blocks (0: the library's)")
     ap.add_argument("--compose", default="auto", choices=list(COMPOSE_NAMES),
                     help="auto: the library's choice (gdn_plan_compose says which); split: prep "
                          "kernel then scan; fused: tile waves inside the scan workgroup, one "
@@ -906,7 +909,8 @@ def main():
                                   spec.hk, spec.hv, spec.dk,
                                   "per-head" if gate == gdn.GATE_HEAD else "per-key-channel",
                                   chunk, ", h0" if spec.h0 else ""),
-                   "tokens": spec.tokens, "arm": args.arm, "composition": composition},
+                   "tokens": spec.tokens, "arm": args.arm, "composition": composition,
+                   "solve_block": args.solve_block or 16},
         "roofline": {"bound": "hbm", "kernel": "gdn_chunk_fwd [%s: %s]" % (composition, kernels[composition]),
                      "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic, "kernel_ms": ms_step,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* Host return codes. */
 typedef enum gdn_status {
@@ -112,6 +112,13 @@ typedef struct gdn_problem {
   int32_t arm;          /* GDN_ARM_MFMA_BF16 or GDN_ARM_FOLD_F32 */
   int32_t compose;      /* GDN_COMPOSE_* */
   int32_t stages;       /* GDN_STAGE_ALL, or PREP / SCAN alone (split composition) */
+  int32_t solve_block;  /* rows of the diagonal blocks of the triangular solve T = (I + A)^-1:
+                           0 = library choice (16), else 8, 16 or 32.  Each diagonal block is
+                           solved by scalar forward substitution, the blocks below it by fp32
+                           MFMA updates against solved blocks; the substitution's work grows
+                           with the block's square, the update steps with the block count (the
+                           rocm-libraries pull 11223 page, section "Levers", item 3).  Results
+                           differ between block sizes by rounding only. */
 } gdn_problem;
 
 /* gdn_validate -- checks a problem description on the host (no device work): every

@@ -39,6 +39,13 @@ gdn_status make_plan(const gdn_problem* p, Plan* out, bool raw) {
       p->compose != GDN_COMPOSE_SEQSPLIT)
     return GDN_E_UNSUPPORTED;
   if (p->stages < 0 || p->stages > (GDN_STAGE_PREP | GDN_STAGE_SCAN)) return GDN_E_UNSUPPORTED;
+  if (!(p->solve_block == 0 || p->solve_block == 8 || p->solve_block == 16 || p->solve_block == 32))
+    return GDN_E_UNSUPPORTED;
+  // the tile stages inside the scan launches (fused, pipelined) solve with the library's
+  // diagonal block only; another block size runs the split composition
+  const bool any_block = p->solve_block == 0 || p->solve_block == kSolveBlock;
+  if (!any_block && (p->compose == GDN_COMPOSE_FUSED || p->compose == GDN_COMPOSE_PIPELINED))
+    return GDN_E_UNSUPPORTED;
   // the fused composition (tile waves inside the scan workgroup) is built for the
   // per-head gate with bf16 inputs on the bf16 arm, and has no separate stages
   if (p->compose == GDN_COMPOSE_FUSED &&
@@ -48,12 +55,13 @@ gdn_status make_plan(const gdn_problem* p, Plan* out, bool raw) {
 
   // the pipelined composition (scan segments carrying the state, the next segment's
   // prep beside each) is built for the per-head gate on fixed-length batches, all stages
-  const bool pipe_ok = p->gate == GDN_GATE_HEAD && p->seq_len > 0 &&
-                       (p->stages == GDN_STAGE_ALL || p->stages == (GDN_STAGE_PREP | GDN_STAGE_SCAN));
+  const bool fixed_all = p->gate == GDN_GATE_HEAD && p->seq_len > 0 &&
+                         (p->stages == GDN_STAGE_ALL || p->stages == (GDN_STAGE_PREP | GDN_STAGE_SCAN));
+  const bool pipe_ok = fixed_all && any_block;
   if (p->compose == GDN_COMPOSE_PIPELINED && !pipe_ok) return GDN_E_UNSUPPORTED;
   // the sequence split (parts scanned side by side, chained through their transitions)
   // additionally needs square states: a transition is a dk x dk state scanned like a value
-  const bool seq_ok = pipe_ok && p->dk == p->dv;
+  const bool seq_ok = fixed_all && p->dk == p->dv;
   if (p->compose == GDN_COMPOSE_SEQSPLIT && !seq_ok) return GDN_E_UNSUPPORTED;
   // raw inputs: the per-head gate, split or pipelined (the row norms pass through the
   // workspace from the prep to the scan; the fused composition has no such stage)
@@ -70,6 +78,7 @@ gdn_status make_plan(const gdn_problem* p, Plan* out, bool raw) {
   pl.total = p->total_tokens;
   pl.gate_channel = p->gate == GDN_GATE_KEY_CHANNEL;
   pl.chunk = p->chunk ? p->chunk : (pl.gate_channel ? 32 : 64);
+  pl.solve_block = p->solve_block ? p->solve_block : kSolveBlock;
   pl.arm_f32 = p->arm == GDN_ARM_FOLD_F32;
   pl.qkv_f32 = p->qkv_dtype == GDN_F32;
   pl.o_f32 = p->o_dtype == GDN_F32;
@@ -267,6 +276,7 @@ static gdn_status chunk_fwd(const gdn_problem* p, const gdn_raw_inputs* raw, con
   prm.prep_ce = prm.seg_ce;
   prm.nscan = (int32_t)((int64_t)pl.n_seq * pl.hv * (pl.dv / 32));
   prm.h0_input = 1;
+  prm.solve_block = pl.solve_block;
   if (raw) {
     prm.raw = 1;
     prm.q_scale = raw->q_scale;

@@ -29,6 +29,9 @@ constexpr int kMaxParts = 4;
 // scanned, the next one being prepared), so their workspace holds a ring of two segments.
 constexpr int kSegTokens = 2048;
 
+// Rows of the triangular solve's diagonal blocks when the problem leaves it to the library.
+constexpr int kSolveBlock = 16;
+
 // Everything a launch needs, resolved on the host from a gdn_problem.
 struct Plan {
   int32_t n_seq, seq_len, hk, hv, dk, dv;
@@ -52,6 +55,7 @@ struct Plan {
                          // sequences longer than two segments), else 0: every chunk its own slot
   int64_t tile_slots;    // chunk slots the tile buffers hold
   int32_t raw;           // 1: raw inputs (gdn_chunk_fwd_raw_inputs)
+  int32_t solve_block;   // rows of the triangular solve's diagonal blocks: 8, 16 or 32
   // workspace carve-up (byte offsets)
   int32_t kq_ws;         // 1: K and Q copied to the workspace in the arm's type
   size_t off_table, off_T, off_P, off_G, off_D, off_K, off_Q, off_carry, off_parts, off_N, bytes;
@@ -114,6 +118,8 @@ struct Params {
   int32_t raw;
   float q_scale, gate_scale;
   float* Nws;
+  // Rows of the diagonal blocks of the triangular solve T = (I + A)^-1: 8, 16 or 32.
+  int32_t solve_block;
 };
 constexpr int kStampSteps = 16, kStampPhases = 8;
 

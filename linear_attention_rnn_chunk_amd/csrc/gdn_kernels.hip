@@ -467,87 +467,174 @@ struct SolveLds {
 // compiler from moving accesses across it.)
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// element (r, q), r >= q, of a C x C lower-triangular matrix held in S as lower tiles
+__device__ __forceinline__ float* tri_at(float* S, int r, int q) {
+  return S + tri(r >> 4, q >> 4) * kTile + (r & 15) * kTP + (q & 15);
+}
+
+// One 16 x 16 tile product on fp32 MFMA 16x16x4, accumulated: acc += X Y with X a lower tile
+// of S read with lanes as its rows (lane (i, g) supplies X[i][4 g + q] to instruction q)
+// and Y given as the accumulator of an earlier product (element q of lane (i, g) is
+// Y[4 g + q][i]), or as a tile of S read by columns.
+__device__ __forceinline__ f32x4 tile_mma_acc(const float* X, const f32x4& Y, f32x4 acc, int i, int g) {
+  const float4 x = *(const float4*)(X + i * kTP + 4 * g);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, Y[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, Y[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, Y[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, Y[3], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ f32x4 tile_mma_tile(const float* X, const float* Y, f32x4 acc, int i, int g) {
+  const float4 x = *(const float4*)(X + i * kTP + 4 * g);
+  const float* y = Y + 4 * g * kTP + i;
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, y[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, y[kTP], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, y[2 * kTP], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, y[3 * kTP], acc, 0, 0, 0);
+  return acc;
+}
+
 // T = (I + A)^-1 for the strictly lower fp32 A held in S (lower tiles; the diagonal
-// tiles' upper parts are ignored), in place: afterwards S holds the lower tiles of T.
-//   diagonal 16 x 16 blocks: forward substitution, one lane per column of a block
-//   off-diagonal blocks, block row by block row:
-//     T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj   (fp32 MFMA 16x16x4)
-// Block row i only reads A's row i and T's earlier rows, so T_i* replaces A_i* once
-// the row is done.  One wave, no workgroup barrier.
-template <int C>
+// tiles' upper parts are ignored), in place: afterwards S holds the lower tiles of T.  A
+// blocked solve with diagonal blocks of B rows (B = 8, 16 or 32):
+//   1. each B x B diagonal block by forward substitution, one lane per column of a block
+//   2. B = 8: the lower-left 8 x 8 block of each diagonal 16 x 16 tile from its two solved
+//      halves, T_10 = -T_11 A_10 T_00 (one lane per element), and its upper right cleared
+//   3. the remaining blocks, block row by block row (16 x 16 tiles; for B = 32 the one
+//      off-diagonal 32 x 32 block of C = 64):
+//        T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj   (fp32 MFMA 16x16x4)
+// Block row i only reads A's row i and T's earlier rows, so T_i* replaces A_i* once the
+// row is done.  One wave, no workgroup barrier.  The substitution's serial depth is B
+// rows, its work B^2 / 2 multiply-adds per lane; smaller blocks move work to the MFMA
+// updates.  (LDS written by some lanes and read by others is ordered by wave_lds_sync.)
+template <int C, int B = 16>
 __device__ __forceinline__ void wave_solve_unit_lower(float* S, int lane) {
-  constexpr int NB = C / 16;
+  static_assert(B == 8 || B == 16 || B == 32, "diagonal block of 8, 16 or 32 rows");
+  static_assert(C % B == 0, "whole diagonal blocks");
+  constexpr int NB = C / 16, NBB = C / B;
   const int i = lane & 15, g = lane >> 4;
   {
-    const int b = (lane >> 4) & (NB - 1), c = lane & 15;
-    float* D = S + tri(b, b) * kTile;
-    float x[16];
+    const int b = (lane / B) % NBB, c = lane % B, r0 = b * B;
+    float x[B];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < B; ++r) {
       float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
       for (int q = 0; 4 * q < r; ++q) {
-        const float4 a = *(const float4*)(D + r * kTP + 4 * q);
+        const float4 a = *(const float4*)tri_at(S, r0 + r, r0 + 4 * q);
         const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (4 * q + e < r) acc = fmaf(-av[e], x[4 * q + e], acc);
       }
       x[r] = acc;
+      // (32 rows: without a point that the finished rows must reach first, the compiler
+      // issues every row's reads up front and holds them all, twice the register file)
+      if constexpr (B == 32)
+        if (r % 4 == 3) asm volatile("" : "+v"(x[r])::"memory");
     }
     wave_lds_sync();
-    if (lane < 16 * NB) {
+    if (lane < NBB * B) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) D[r * kTP + c] = x[r];
+      for (int r = 0; r < B; ++r)
+        if (B < 32 || r >= 16 || c < 16) *tri_at(S, r0 + r, r0 + c) = x[r];  // (stored tiles only)
     }
     wave_lds_sync();
   }
+  if constexpr (B == 8) {
+    const int r = lane >> 3, c = lane & 7;
 #pragma unroll
-  for (int ib = 1; ib < NB; ++ib) {
-    f32x4 R[NB];
+    for (int d = 0; d < NB; ++d) {
+      float* Dt = S + tri(d, d) * kTile;
+      float z = 0.f;
 #pragma unroll
-    for (int jb = 0; jb < ib; ++jb) {
-      // Z = sum_m A_{ib,m} T_{m,jb}: instruction q pairs k = 4 g + q of lane group g
-      f32x4 Z = zero4();
+      for (int m = 0; m < 8; ++m)  // Z = A_10 T_00 (T_00 lower: m >= c)
+        if (m >= c) z = fmaf(Dt[(8 + r) * kTP + m], Dt[m * kTP + c], z);
+      wave_lds_sync();
+      Dt[(8 + r) * kTP + c] = z;
+      wave_lds_sync();
+      float t = 0.f;
 #pragma unroll
-      for (int m = jb; m < ib; ++m) {
-        const float4 a = *(const float4*)(S + tri(ib, m) * kTile + i * kTP + 4 * g);
-        const float* tm = S + tri(m, jb) * kTile + 4 * g * kTP + i;
-        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, tm[0], Z, 0, 0, 0);
-        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, tm[kTP], Z, 0, 0, 0);
-        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, tm[2 * kTP], Z, 0, 0, 0);
-        Z = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, tm[3 * kTP], Z, 0, 0, 0);
+      for (int m = 0; m < 8; ++m)  // T_10 = -T_11 Z (T_11 lower: m <= r)
+        if (m <= r) t = fmaf(Dt[(8 + r) * kTP + 8 + m], Dt[(8 + m) * kTP + c], t);
+      wave_lds_sync();
+      Dt[(8 + r) * kTP + c] = -t;
+      Dt[r * kTP + 8 + c] = 0.f;  // the tile's upper right stays zero for the block updates
+      wave_lds_sync();
+    }
+  }
+  if constexpr (B <= 16) {
+#pragma unroll
+    for (int ib = 1; ib < NB; ++ib) {
+      f32x4 R[NB];
+#pragma unroll
+      for (int jb = 0; jb < ib; ++jb) {
+        // Z = sum_m A_{ib,m} T_{m,jb}
+        f32x4 Z = zero4();
+#pragma unroll
+        for (int m = jb; m < ib; ++m) Z = tile_mma_tile(S + tri(ib, m) * kTile, S + tri(m, jb) * kTile, Z, i, g);
+        // T_{ib,jb} = -T_{ib,ib} Z
+        R[jb] = tile_mma_acc(S + tri(ib, ib) * kTile, Z, zero4(), i, g);
       }
-      // T_{ib,jb} = -T_{ib,ib} Z: Z's accumulator element q is its row 4 g + q
-      const float4 d = *(const float4*)(S + tri(ib, ib) * kTile + i * kTP + 4 * g);
-      f32x4 t = zero4();
-      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.x, Z[0], t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.y, Z[1], t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.z, Z[2], t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x4f32(d.w, Z[3], t, 0, 0, 0);
-      R[jb] = t;
+      wave_lds_sync();
+#pragma unroll
+      for (int jb = 0; jb < ib; ++jb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[tri(ib, jb) * kTile + (4 * g + j) * kTP + i] = -R[jb][j];
+      wave_lds_sync();
+    }
+  } else if constexpr (C == 64) {
+    // the off-diagonal 32 x 32 block (tiles 2, 3 by 0, 1): Z = A_10 T_00 at 32-row
+    // granularity (T_00 lower: its tile (0, 1) is zero), then T_10 = -T_11 Z
+    f32x4 Z[2][2], R[2][2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        Z[it][jt] = zero4();
+#pragma unroll
+        for (int m = jt; m < 2; ++m)
+          Z[it][jt] = tile_mma_tile(S + tri(2 + it, m) * kTile, S + tri(m, jt) * kTile, Z[it][jt], i, g);
+      }
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      R[0][jt] = tile_mma_acc(S + tri(2, 2) * kTile, Z[0][jt], zero4(), i, g);
+      R[1][jt] = tile_mma_acc(S + tri(3, 3) * kTile, Z[1][jt],
+                              tile_mma_acc(S + tri(3, 2) * kTile, Z[0][jt], zero4(), i, g), i, g);
     }
     wave_lds_sync();
 #pragma unroll
-    for (int jb = 0; jb < ib; ++jb)
+    for (int it = 0; it < 2; ++it)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[tri(ib, jb) * kTile + (4 * g + j) * kTP + i] = -R[jb][j];
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[tri(2 + it, jt) * kTile + (4 * g + j) * kTP + i] = -R[it][jt][j];
     wave_lds_sync();
   }
+}
+
+// The solve with the diagonal block size chosen at run time (8, 16 or 32 rows; anything else
+// is 16).
+template <int C>
+__device__ __forceinline__ void wave_solve(float* S, int lane, int rows) {
+  if (rows == 8) wave_solve_unit_lower<C, 8>(S, lane);
+  else if (rows == 32) wave_solve_unit_lower<C, 32>(S, lane);
+  else wave_solve_unit_lower<C, 16>(S, lane);
 }
 
 // From the lower tiles of the two chunk products, oriented with lanes as rows (element j
 // of tile (rt, st) in lane (i, g) is row r = 16 rt + i, column s = 16 st + 4 g + j):
 //   A = tril_strict(beta_r e^{G_r - G_s} KK),  P = tril(e^{G_r - G_s} QK), rows r < L
 // (per-channel gate: the exponentials are already inside the products, G unused);
-// then T = (I + A)^-1 in this wave's LDS S, and T, P stored as scan fragments.
+// then T = (I + A)^-1 in this wave's LDS S (diagonal blocks of solve_rows rows), and T, P stored
+// as scan fragments.
 // Raw inputs (Nk, Nq non-null: 1 / |k_r| and q_scale / |q_r| of the chunk's rows in LDS):
 // the products of the raw rows become those of the normalised rows, A_rs by Nk_r Nk_s and
 // P_rs by Nq_r Nk_s (without them every factor is exactly 1, so the bits are unchanged).
 template <class Arm, int C, bool KDA>
 __device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, const float* Gs,
                                            const float* Bs, typename Arm::T* Tout,
-                                           typename Arm::T* Pout, int L, int lane,
+                                           typename Arm::T* Pout, int L, int lane, int solve_rows,
                                            const float* Nk = nullptr, const float* Nq = nullptr) {
   constexpr int NT = C / 16;
   const int i = lane & 15, g = lane >> 4;
@@ -586,7 +673,7 @@ __device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, c
       Arm::st8(Pout + (tile_frag_index(mt, sb) * 64 + lane) * 8, accP[tri(mt, 2 * sb)], hi);
     }
   wave_lds_sync();
-  wave_solve_unit_lower<C>(S, lane);
+  wave_solve<C>(S, lane, solve_rows);
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
@@ -845,7 +932,8 @@ __device__ __forceinline__ bool prep_fetch(const Params& p, int64_t slot, int kh
 }
 
 template <class Arm, int DK, int C, bool QF32>
-__device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, C, QF32>& U, int lane, float* S) {
+__device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, C, QF32>& U, int lane, float* S,
+                                            int solve_rows) {
   using SL = SolveLds<C>;
   constexpr int NT = C / 16, NTRI = SL::NTRI, NBK = DK / 32;
   const int i = lane & 15, g = lane >> 4;
@@ -881,7 +969,7 @@ __device__ __forceinline__ void prep_finish(const Params& p, const PrepUnit<DK, 
   tile_products<Arm, DK, C, QF32>(U.R, accA, accP);
   typedef typename Arm::T T;
   const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
-  wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, Nk, Nq);
+  wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, solve_rows, Nk, Nq);
   if (bad) atomicOr(p.status, bad);
 }
 
@@ -911,7 +999,7 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
   if (j >= group || !prep_slot(p, m, slot)) return;
   PrepUnit<DK, C, QF32> U;
   if (prep_fetch<DK, C, QF32>(p, slot, kh, j, lane, U))
-    prep_finish<Arm, DK, C, QF32>(p, U, lane, (float*)gdn_smem + w * SL::FLOATS);
+    prep_finish<Arm, DK, C, QF32>(p, U, lane, (float*)gdn_smem + w * SL::FLOATS, p.solve_block);
 }
 
 // The prep of the next scan segment, run by the workgroups of a pipelined scan launch
@@ -923,7 +1011,9 @@ __global__ __launch_bounds__(256) void gdn_prep_head(Params p) {
 // K and Q and forms K K^T and Q K^T once, then gates, solves and stores the tiles of each
 // value head of the key head's group from a copy of the two products: the same
 // instructions on the same values as the prep kernel, so the same bits.  (fp32 inputs or
-// operands: units of one value head, like the prep kernel's waves.)
+// operands: units of one value head, like the prep kernel's waves.)  The solve here is
+// built for the library's diagonal block only (kSolveBlock rows): the scan kernel's
+// registers leave no room for the other sizes' code, so the composition runs only with it.
 template <class Arm, int DK, int C, bool QF32>
 __device__ __forceinline__ void prep_role(const Params& p) {
   using SL = SolveLds<C>;
@@ -946,7 +1036,7 @@ __device__ __forceinline__ void prep_role(const Params& p) {
       int64_t slot;
       PrepUnit<DK, C, QF32> U;
       if (prep_slot(p, 8 * k + x, slot) && prep_fetch<DK, C, QF32>(p, slot, h / group, h % group, lane, U))
-        prep_finish<Arm, DK, C, QF32>(p, U, lane, S);
+        prep_finish<Arm, DK, C, QF32>(p, U, lane, S, kSolveBlock);
     }
     return;
   }
@@ -1014,7 +1104,8 @@ __device__ __forceinline__ void prep_role(const Params& p) {
         accP[t] = P0[t];
       }
       const int64_t tofs = (slot * p.hv + h0 + j) * (int64_t)tile_elems(C);
-      wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, Nk, Nq);
+      wave_tiles<Arm, C, false>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, kSolveBlock, Nk,
+                                Nq);
     }
     if (bad) atomicOr(p.status, bad);
   }
@@ -1155,7 +1246,7 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
         }
     }
     const int64_t tofs = (slot * p.hv + h) * (int64_t)tile_elems(C);
-    wave_tiles<Arm, C, true>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane);
+    wave_tiles<Arm, C, true>(accA, accP, S, Gs, Bs, (T*)p.Tws + tofs, (T*)p.Pws + tofs, L, lane, p.solve_block);
   }
   if (bad) atomicOr(p.status, bad);
 }
@@ -2147,7 +2238,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       bad |= tile_sweep<C>(xl, bl, L, ln, Gs, Bs, p);
       T* Tout = (T*)(exch + SL::TT + (cu & 1) * SL::TILEB);
       T* Pout = (T*)(exch + SL::TP + (cu & 1) * SL::TILEB);
-      wave_tiles<Arm, C, false>(accA, accP, Sv, Gs, Bs, Tout, Pout, L, ln);
+      wave_tiles<Arm, C, false>(accA, accP, Sv, Gs, Bs, Tout, Pout, L, ln, kSolveBlock);
     };
     // every role passes nch + 1 barriers: the first one, then one per step
     int passed = 0;

@@ -37,6 +37,7 @@ EXPORTS = ("gdn_validate", "gdn_workspace_bytes", "gdn_plan_compose", "gdn_chunk
            "gdn_status_string", "gdn_abi_version")
 # the largest workspace gdn_chunk_fwd_noalloc serves (its per-device array)
 NOALLOC_WORKSPACE_BYTES = 64 << 20
+ABI_VERSION = 2  # the gdn_problem layout above (GDN_ABI_VERSION)
 
 
 class Problem(ctypes.Structure):
@@ -45,7 +46,7 @@ class Problem(ctypes.Structure):
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("arm", ctypes.c_int32), ("compose", ctypes.c_int32),
-                ("stages", ctypes.c_int32)]
+                ("stages", ctypes.c_int32), ("solve_block", ctypes.c_int32)]
 
 
 class RawInputs(ctypes.Structure):
@@ -117,6 +118,9 @@ def load():
             lib.gdn_status_string.argtypes = [ctypes.c_uint32]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_abi_version.restype = ctypes.c_int32
+            if lib.gdn_abi_version() != ABI_VERSION:
+                raise RuntimeError("%s has ABI version %d, this binding expects %d: rebuild it"
+                                   % (_path, lib.gdn_abi_version(), ABI_VERSION))
             _lib = lib
     return _lib
 
@@ -135,10 +139,10 @@ def abi_version() -> int:
 
 def make_problem(n_seq, total_tokens, seq_len, hk, hv, dk, dv, gate=GATE_HEAD, chunk=0,
                  qkv_dtype=BF16, o_dtype=BF16, arm=ARM_MFMA_BF16, compose=COMPOSE_AUTO,
-                 stages=STAGE_ALL) -> Problem:
+                 stages=STAGE_ALL, solve_block=0) -> Problem:
     return Problem(int(n_seq), int(total_tokens), int(seq_len), int(hk), int(hv), int(dk), int(dv),
                    int(gate), int(chunk), int(qkv_dtype), int(o_dtype), int(arm), int(compose),
-                   int(stages))
+                   int(stages), int(solve_block))
 
 
 def validate(prob: Problem) -> int:
@@ -219,7 +223,8 @@ def chunk_fwd_noalloc_raw(prob: Problem, q, k, v, g, beta, h0, cu_seqlens, o, hT
 
 def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm: str = "bf16",
               o_dtype: Optional[torch.dtype] = None, compose: str = "auto", want_hT: bool = True,
-              check: bool = True, workspace: Optional[torch.Tensor] = None, raw: Optional[tuple] = None):
+              check: bool = True, workspace: Optional[torch.Tensor] = None, raw: Optional[tuple] = None,
+              solve_block: int = 0):
     """Chunkwise gated delta-rule prefill on the current device and stream.
 
     With ``raw = (q_scale, gate_scale)`` the inputs are the raw per-token values
@@ -231,7 +236,8 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm
     Packed batch (cu_seqlens int32 [N+1]): the same with B = 1 (or no batch axis) and
     h0 [N, HV, DK, DV].  Returns (o [..., HV, DV], hT [N, HV, DK, DV] or None, status
     int32[1] on the device).  With ``check`` the stream is synchronised and any device
-    status bit raises GdnStatusError.
+    status bit raises GdnStatusError.  ``solve_block`` (8, 16, 32; 0 = library choice) sets the
+    rows of the triangular solve's diagonal blocks.
     """
     if q.dim() == 3:
         q, k, v, g, beta = (x.unsqueeze(0) for x in (q, k, v, g, beta))
@@ -267,7 +273,7 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk: int = 0, arm
         raise ValueError("h0 must be float32 [N, HV, DK, DV]")
     odt = o_dtype or q.dtype
     prob = make_problem(n_seq, B * T, seq_len, HK, HV, DK, DV, gate, chunk, _DT[q.dtype], _DT[odt],
-                        _ARM[arm], _COMPOSE[compose])
+                        _ARM[arm], _COMPOSE[compose], solve_block=solve_block)
     rc = validate(prob)
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_validate")

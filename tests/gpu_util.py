@@ -36,12 +36,12 @@ def device_inputs(inp):
     return dict(q=shp(q), k=shp(k), v=shp(v), g=shp(g), beta=shp(b), h0=h0, cu_seqlens=cu)
 
 
-def run_gpu(inp, arm="bf16", chunk=None, compose="auto", o_dtype=None, d=None, check=True):
+def run_gpu(inp, arm="bf16", chunk=None, compose="auto", o_dtype=None, d=None, check=True, solve_block=0):
     d = d or device_inputs(inp)
     odt = o_dtype or ODT[arm]
     o, hT, st = gdn.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
                               chunk=chunk if chunk is not None else inp.spec.chunk, arm=arm,
-                              o_dtype=odt, compose=compose, check=check)
+                              o_dtype=odt, compose=compose, check=check, solve_block=solve_block)
     tok = inp.spec.tokens
     o = o.reshape(tok, inp.spec.hv, inp.spec.dv)
     return o, hT, st

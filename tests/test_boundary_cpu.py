@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert gdn.abi_version() == 1
+    assert gdn.abi_version() == gdn.ABI_VERSION == 2
     assert gdn.error_string(0) == "ok"
     for c in range(1, 7):
         assert gdn.error_string(c) != "unknown error code"
@@ -89,6 +89,20 @@ def P(**kw):
     (dict(compose=gdn.COMPOSE_SEQSPLIT, gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=gdn.COMPOSE_SEQSPLIT, n_seq=3, seq_len=0), gdn.GDN_E_UNSUPPORTED),
     (dict(compose=gdn.COMPOSE_SEQSPLIT, stages=gdn.STAGE_PREP), gdn.GDN_E_UNSUPPORTED),
+    # the solve's diagonal block: 8, 16 or 32 rows (0: the library's); the tile stages inside
+    # scan launches (fused, pipelined) are built for 16 rows only
+    (dict(solve_block=8), gdn.GDN_OK),
+    (dict(solve_block=16), gdn.GDN_OK),
+    (dict(solve_block=32, chunk=32), gdn.GDN_OK),
+    (dict(solve_block=8, gate=gdn.GATE_KEY_CHANNEL, chunk=32), gdn.GDN_OK),
+    (dict(solve_block=32, compose=gdn.COMPOSE_SEQSPLIT), gdn.GDN_OK),
+    (dict(solve_block=16, compose=gdn.COMPOSE_PIPELINED), gdn.GDN_OK),
+    (dict(solve_block=16, compose=gdn.COMPOSE_FUSED), gdn.GDN_OK),
+    (dict(solve_block=4), gdn.GDN_E_UNSUPPORTED),
+    (dict(solve_block=64), gdn.GDN_E_UNSUPPORTED),
+    (dict(solve_block=-16), gdn.GDN_E_UNSUPPORTED),
+    (dict(solve_block=8, compose=gdn.COMPOSE_PIPELINED), gdn.GDN_E_UNSUPPORTED),
+    (dict(solve_block=32, compose=gdn.COMPOSE_FUSED), gdn.GDN_E_UNSUPPORTED),
 ])
 def test_validate_refusals(kw, code):
     assert gdn.validate(P(**kw)) == code
@@ -103,6 +117,10 @@ def test_plan_compose_host_rules():
     assert gdn.plan_compose(P(gate=gdn.GATE_KEY_CHANNEL, chunk=32)) == gdn.COMPOSE_SPLIT
     assert gdn.plan_compose(P(n_seq=3, seq_len=0)) == gdn.COMPOSE_SPLIT
     assert gdn.plan_compose(P(compose=gdn.COMPOSE_AUTO)) in (gdn.COMPOSE_SPLIT, gdn.COMPOSE_PIPELINED)
+    # another diagonal block of the solve keeps the tile stage in its own kernel
+    for sb in (8, 32):
+        assert gdn.plan_compose(P(n_seq=8, total_tokens=8 * 32768, seq_len=32768, hk=16, hv=32,
+                                  solve_block=sb)) == gdn.COMPOSE_SPLIT
     with pytest.raises(gdn.GdnError):
         gdn.plan_compose(P(dk=96))
     lib = gdn.load()

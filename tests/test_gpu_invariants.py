@@ -22,10 +22,13 @@ pytestmark = pytest.mark.gpu
 
 
 # ------------------------------------------------------------ tile level -----
+# every diagonal block of the solve (8, 16, 32 rows); 8 rows is the size at which a missing
+# wait between one lane's LDS write and another lane's read shows first
 @pytest.mark.parametrize("arm,tol", [("bf16", 1e-2), ("f32", 1e-5)])
-@pytest.mark.parametrize("gate,law,C", [("head", "clip5", 64), ("channel", "uniform5", 32),
+@pytest.mark.parametrize("gate,law,C", [("head", "clip5", 64), ("head", "clip5", 32), ("channel", "uniform5", 32),
                                         ("channel", "uniform05", 32)])
-def test_solve_and_P_tiles_match_chunk_oracle(arm, tol, gate, law, C):
+@pytest.mark.parametrize("sb", [8, 16, 32])
+def test_solve_and_P_tiles_match_chunk_oracle(sb, arm, tol, gate, law, C):
     spec = inputs.Spec("tiles", (150,), 1, 2, 64, 64, qkv_dtype="bf16", gate=gate, gate_law=law,
                        h0=True, chunk=C, seed=21)
     inp = inputs.make(spec)
@@ -34,7 +37,7 @@ def test_solve_and_P_tiles_match_chunk_oracle(arm, tol, gate, law, C):
                             gdn.GATE_KEY_CHANNEL if gate == "channel" else gdn.GATE_HEAD, C,
                             gdn.BF16, gdn.F32 if arm == "f32" else gdn.BF16,
                             gdn.ARM_FOLD_F32 if arm == "f32" else gdn.ARM_MFMA_BF16,
-                            gdn.COMPOSE_SPLIT, gdn.STAGE_PREP)
+                            gdn.COMPOSE_SPLIT, gdn.STAGE_PREP, solve_block=sb)
     ws = torch.zeros(gdn.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     o = torch.empty((1, spec.tokens, 2, 64), dtype=torch.float32 if arm == "f32" else torch.bfloat16,
@@ -52,7 +55,8 @@ def test_solve_and_P_tiles_match_chunk_oracle(arm, tol, gate, law, C):
         et = rel(Tg[ci, h].float().cpu().numpy(), t["T"])
         ep = rel(Pg[ci, h].float().cpu().numpy(), t["P"])
         worst_t, worst_p = max(worst_t, et), max(worst_p, ep)
-    print("tiles %s %s: worst rel-L2 T %.3e P %.3e" % (arm, law, worst_t, worst_p))
+    print("tiles solve_block=%d C=%d %s %s: worst rel-L2 T %.3e P %.3e" % (sb, C, arm, law, worst_t, worst_p),
+          flush=True)
     assert worst_t <= tol and worst_p <= tol
 
 

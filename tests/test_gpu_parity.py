@@ -11,8 +11,8 @@ from tests.gpu_util import BOUND, oracle_ref, rel, run_gpu, to_np64
 pytestmark = pytest.mark.gpu
 
 
-def _check(inp, arm, chunk=None, label=""):
-    o, hT, _ = run_gpu(inp, arm=arm, chunk=chunk)
+def _check(inp, arm, chunk=None, label="", solve_block=0):
+    o, hT, _ = run_gpu(inp, arm=arm, chunk=chunk, solve_block=solve_block)
     o_ref, h_ref = oracle_ref(inp)
     eo, eh = rel(to_np64(o), o_ref), rel(to_np64(hT), h_ref)
     print("%s arm=%s chunk=%s rel-L2 o=%.3e hT=%.3e" % (label or inp.spec.name, arm, chunk, eo, eh),
@@ -81,6 +81,20 @@ def test_unit_key_equal_query_returns_value(T, gate, law, arm):
     print("o=v T=%d %s/%s arm=%s: rel-L2 o-v %.3e, vs oracle o %.3e hT %.3e" % (T, gate, law, arm, ev, eo, eh),
           flush=True)
     assert ev <= BOUND[arm] and eo <= BOUND[arm] and eh <= BOUND[arm], (ev, eo, eh)
+
+
+# The triangular solve's diagonal block (8, 16, 32 rows) changes only the rounding: every
+# size against the oracle, on packed ragged sequences (an empty one, chunk tails of 7 and 1
+# rows) with beta at 1 (the largest off-diagonal entries of A) and at its random law.
+@pytest.mark.parametrize("arm", ["f32", "bf16"])
+@pytest.mark.parametrize("gate,law,C", [("head", "clip5", 64), ("head", "full", 32), ("channel", "uniform5", 32)])
+@pytest.mark.parametrize("beta_law", ["one", "sigmoid"])
+@pytest.mark.parametrize("sb", [8, 16, 32])
+def test_solve_block_sweep(sb, beta_law, gate, law, C, arm):
+    spec = inputs.Spec("solve-block", (199, 0, 1, 71), 2, 4, 64, 64, qkv_dtype="bf16", gate=gate, gate_law=law,
+                       h0=True, chunk=C, packed=True, beta_law=beta_law, seed=1200 + sb + C)
+    _check(inputs.make(spec), arm, label="solve_block=%d C=%d %s/%s beta=%s" % (sb, C, gate, law, beta_law),
+           solve_block=sb)
 
 
 @pytest.mark.parametrize("arm", ["f32", "bf16"])
