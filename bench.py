@@ -96,13 +96,14 @@ def composition_overhead_bytes(spec, chunk):
 
 
 # the source file holding each workload's kernels and their launch code
-KERNEL_SOURCE = {"hybrid": "gdn_kernels.hip", "decode": "gdn_decode.hip"}
+KERNEL_SOURCE = {"decode": "gdn_decode.hip"}  # every prefill workload: gdn_kernels.hip
 
 
 def source_digest(label="hybrid"):
     """Digest of a kernel source's code: comments and whitespace are dropped, so an edit
     of the comments alone keeps the counters taken on that code valid."""
-    with open(os.path.join(ROOT, "linear_attention_rnn_chunk_amd", "csrc", KERNEL_SOURCE[label])) as fh:
+    with open(os.path.join(ROOT, "linear_attention_rnn_chunk_amd", "csrc",
+                           KERNEL_SOURCE.get(label, "gdn_kernels.hip"))) as fh:
         src = fh.read()
     code = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     code = re.sub(r"//[^\n]*", " ", code)
@@ -287,7 +288,7 @@ def summarize_counters(pmc_dir, kt_dir, cmd, title, label, composition, calls):
              "# waves_per_cu = SQ_WAVE_CYCLES x 4 / (GRBM_GUI_ACTIVE / 8 x %d CUs): mean resident waves "
              "per CU over the launch, idle CUs included" % N_CU,
              "composition: %s" % composition,
-             "source_digest: %s" % source_digest(label if label == "decode" else "hybrid")]
+             "source_digest: %s" % source_digest(label)]
     tot = {}
     for k in per:
         for n, v in per[k].items():
@@ -715,8 +716,9 @@ def main():
                                      label, composition, calls)
             out.append(("mfma_counters_%s.txt" % label, txt))
         if args.summarize_launches:
+            # (the per-dispatch trace of the kernel-trace run)
             txt = summarize_launches(args.summarize_launches,
-                                     "cd /tmp && rocprofv3 --kernel-trace -d <out>/prof_lt -o lt -f csv -- " + run,
+                                     "cd /tmp && rocprofv3 --kernel-trace --stats -d <out>/prof_kt -o kt -f csv -- " + run,
                                      title, composition)
             out.append(("launches_%s.txt" % label, txt))
         if args.summarize_profiles:
