@@ -6,13 +6,13 @@ over the hybrid-model GDN layer: B=1, T=32768, 16 key heads / 48 value heads,
 dk = dv = 128, bf16 q/k/v, fp32 gate and beta, chunk 64, nonzero h0 (synthetic
 seeded inputs, resident in HBM before timing).  Prints one JSON line.
 
-Per-kernel durations come from HIP events recorded on the library's stream
-around each stage call inside the timed loop (the step is issued as a PREP call
-then a SCAN call on the same workspace, which is exactly the work of one full
-call).  A 1 GiB scratch write before each step (outside its events) starts every
-step cache-cold; the headline is the median step, with the minimum and a
-warm-cache median beside it.  The oracle (fp64 token-serial, OpenMP) is timed on
-a bounded sample of the same workload on the host cores.
+A step is one whole gdn_chunk_fwd call in the library's own composition for the
+workload, between HIP events recorded on the library's stream.  A 1 GiB scratch
+write before each step (outside its events) starts every step cache-cold; the
+headline is the median step, with the minimum and a warm-cache median beside it.
+The split composition's two stages are then timed one by one in a second pass
+(per-kernel figures).  The oracle (fp64 token-serial, OpenMP) is timed on a
+bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
