@@ -346,9 +346,12 @@ def measured_peaks(dev):
 
 
 def cpu_baseline(inp, budget_s):
-    """Oracle on the first N tokens of every value head (N calibrated to ~budget_s)."""
+    """Oracle on the first N tokens of the first sequence, every value head (N calibrated to
+    ~budget_s).  Raw-input workloads run the input-side oracle in front of it, as the
+    library's raw entry point does."""
     import numpy as np
     import oracle
+    from oracle import prepare
 
     spec = inp.spec
     q64, k64, v64 = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
@@ -358,8 +361,12 @@ def cpu_baseline(inp, budget_s):
     def run(ntok):
         sl = slice(0, ntok)
         t0 = time.perf_counter()
-        oracle.serial_fwd(q64[sl], k64[sl], v64[sl], g64[sl], b64[sl],
-                          None if h064 is None else h064[:1], seq_start=np.array([0, ntok]))
+        h = None if h064 is None else h064[:1]
+        if getattr(spec, "raw", False):
+            prepare.raw_fwd(q64[sl], k64[sl], v64[sl], g64[sl], b64[sl], inp.meta["q_scale"],
+                            inp.meta["gate_scale"], h, seq_start=np.array([0, ntok]))
+        else:
+            oracle.serial_fwd(q64[sl], k64[sl], v64[sl], g64[sl], b64[sl], h, seq_start=np.array([0, ntok]))
         return time.perf_counter() - t0
 
     cal = min(128, L0)
@@ -368,8 +375,10 @@ def cpu_baseline(inp, budget_s):
     secs = run(ntok)
     cores = min(oracle.max_threads(), spec.hv)
     return dict(value=ntok / secs, unit="tokens/s", cores=cores, kind="oracle",
-                sample="fp64 token-serial oracle, all %d value heads of the hybrid layer over its "
-                       "first %d tokens (%.1f s)" % (spec.hv, ntok, secs))
+                sample="fp64 token-serial oracle%s, all %d value heads of the %s workload's first "
+                       "sequence over its first %d tokens (%.1f s)"
+                       % (" after the input-side oracle" if getattr(spec, "raw", False) else "", spec.hv,
+                          spec.name, ntok, secs))
 
 
 def copy_probe(mib, dev):
