@@ -1455,11 +1455,15 @@ struct ScanLds {
   static constexpr int FIXED = TL ? SS + SSB : EXCH;
   static constexpr int BYTES = NBUF * BUF + FIXED;
   static_assert(NBUF >= 2 && BYTES <= LDS_MAX, "scan LDS budget");
-  // loader copy instructions per chunk
-  static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;
+  // Loader copy instructions per chunk.  The loader's copy loops run over exactly these
+  // counts, and its vmcnt waits are ND (plus NRAW for raw inputs): one definition for both.
+  static constexpr int NOPS = (KDA ? 2 : 1) + (QR ? 1 : 0);  // C x DK operands (K, e^{G_C-G} K, Q)
+  static constexpr int NDK = OpLayout<Arm, DK>::template bytes<C>() / 1024;  // per operand
   static constexpr int NDT = tile_elems(C) * (int)sizeof(T) / 1024;  // T or P of a chunk
   static constexpr int NDV = C * WC * ESZV / 1024;
-  static constexpr int ND = ((KDA ? 2 : 1) + (QR ? 1 : 0)) * NDK + (TL ? 0 : NDT) + NDV + (KDA ? 1 : 2) + NDD;
+  static constexpr int NROW = KDA ? 1 : 2;  // 4-byte rows: beta, and the gate for the per-head gate
+  static constexpr int NRAW = 2;            // raw inputs: the two row-factor rows
+  static constexpr int ND = NOPS * NDK + (TL ? 0 : NDT) + NDV + NROW + NDD;
   static_assert(NDK * 1024 == OpLayout<Arm, DK>::template bytes<C>(), "K copy granularity");
   static_assert(NDT * 1024 == tile_elems(C) * (int)sizeof(T), "T / P copy granularity");
   static_assert(NDV * 1024 == C * WC * ESZV, "V copy granularity");
@@ -1635,7 +1639,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       const char* vsrc = (const char*)p.v + (t0 * hvs + h) * (int64_t)(DV * ESZV) + WC * slice * ESZV;
       if (L == C) {  // uniform
 #pragma unroll
-        for (int w = 0; w < (KDA ? 2 : 1) + (SL::QR ? 1 : 0); ++w) {
+        for (int w = 0; w < SL::NOPS; ++w) {
           const char* src = (const char*)(w == (KDA ? 2 : 1) ? src_q(ci) : src_k(ci, w));
           const int dst = w == (KDA ? 2 : 1) ? SL::QO : (KDA && w ? SL::KH : SL::KY);
 #pragma unroll
@@ -1645,7 +1649,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
         for (int k = 0; k < SL::NDV; ++k) dma16(vsrc + voff[k], B + SL::VV + k * 1024);
       } else {  // partial last chunk: rows past the end re-read its last row (in bounds)
 #pragma unroll
-        for (int w = 0; w < (KDA ? 2 : 1) + (SL::QR ? 1 : 0); ++w) {
+        for (int w = 0; w < SL::NOPS; ++w) {
           const T* src = w == (KDA ? 2 : 1) ? src_q(ci) : src_k(ci, w);
           const int dst = w == (KDA ? 2 : 1) ? SL::QO : (KDA && w ? SL::KH : SL::KY);
 #pragma unroll
@@ -1668,6 +1672,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       }
       // gate and beta of row min(lane, L - 1); the sweep masks rows past the end
       const int64_t e = (t0 + (lane < L ? lane : L - 1)) * hvs + h;
+      static_assert(SL::NROW == (KDA ? 1 : 2), "row copies below");
       if constexpr (!KDA) dma4(p.g + e, B + SL::GX);
       dma4(p.beta + e, B + SL::GB);
       if constexpr (KDA) {
@@ -1675,7 +1680,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
 #pragma unroll
         for (int m = 0; m < SL::NDD; ++m) dma4(D + min(lane + 64 * m, DK - 1), B + SL::DC + m * 256);
       } else {
-        if (p.raw) {  // the chunk's row norms, as the prep stored them (two more copies)
+        if (p.raw) {  // the chunk's row norms, as the prep stored them (NRAW more copies)
+          static_assert(SL::NRAW == 2, "row-factor copies below");
           const float* N = p.Nws + ((slot0 + ci) * p.hk + kh) * (int64_t)(2 * C) + (lane < C ? lane : C - 1);
           dma4(N, B + SL::NR);
           dma4(N + C, B + SL::NR + 4 * C);
@@ -1733,13 +1739,13 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     // one chunk's copies (LA - CL <= 1) may stay in flight past a wait, so each wait
     // allows either ND outstanding copies (when a later chunk was issued) or none.
     static_assert(LA - CL <= 1, "one chunk in flight beyond the completed window");
-    // (raw inputs: two more copies per chunk, the row norms)
+    // (raw inputs: NRAW more copies per chunk, the row norms)
     const bool xr = !KDA && p.raw;
 #pragma unroll
     for (int j = 0; j < LA; ++j)
       if (j < nch) issue(j);
     if (LA > CL && nch > LA - 1) {
-      if (xr) wait_vm<(LA > CL ? SL::ND + 2 : 0)>();
+      if (xr) wait_vm<(LA > CL ? SL::ND + SL::NRAW : 0)>();
       else wait_vm<(LA > CL ? SL::ND : 0)>();
     } else {
       wait_vm<0>();
@@ -1756,7 +1762,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       // chunk ci + CL complete: all copies but this step's, which stay in flight across
       // the barrier
       if (LA > CL && more) {
-        if (xr) wait_vm<(LA > CL ? SL::ND + 2 : 0)>();
+        if (xr) wait_vm<(LA > CL ? SL::ND + SL::NRAW : 0)>();
         else wait_vm<(LA > CL ? SL::ND : 0)>();
       } else {
         wait_vm<0>();
