@@ -33,6 +33,17 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 
 METRIC = "GDN chunk-prefill tokens/s per layer (HV=48,T=32k,d=128); MFMA % of peak"
 
+# Context only (not a baseline of this metric): the stratat.com pull #1296 page, section
+# "Measured verdict on gfx1100", times an engine's whole GDN recurrence for a 32k-token
+# prefill on a Radeon 7900 XTX, over a number of layers it does not state, so no per-layer
+# rate follows from these figures.
+GFX1100_CONTEXT = {
+    "source": "stratat.com pull #1296, 'Measured verdict on gfx1100' (Radeon 7900 XTX, nightly ROCm)",
+    "workload": "engine GDN recurrence, 32k-token prefill, HV=48, state 128; layer count not stated",
+    "serial_cols_pipe_ms": 1318, "wy_rocwmma_arm_ms_equivalent": 3050, "wy_fma_arm_ms": 189878,
+    "comparable": False,
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -956,6 +967,8 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None
+    if args.config == "hybrid":
+        rec["context_gfx1100"] = GFX1100_CONTEXT
     print(json.dumps(rec), flush=True)
 
 
