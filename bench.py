@@ -111,13 +111,15 @@ KERNEL_SOURCE = {"decode": "gdn_decode.hip"}  # every prefill workload: gdn_kern
 
 
 def source_digest(label="hybrid"):
-    """Digest of a kernel source's code: comments and whitespace are dropped, so an edit
-    of the comments alone keeps the counters taken on that code valid."""
+    """Digest of a kernel source's code: comments, whitespace and the measurement build's
+    stamp statements (GDN_STAMP, empty in the product library) are dropped, so an edit of
+    those alone keeps the counters taken on that code valid."""
     with open(os.path.join(ROOT, "linear_attention_rnn_chunk_amd", "csrc",
                            KERNEL_SOURCE.get(label, "gdn_kernels.hip"))) as fh:
         src = fh.read()
     code = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     code = re.sub(r"//[^\n]*", " ", code)
+    code = re.sub(r"(if \(u == 0\) )?GDN_STAMP\([^;]*\);", " ", code)
     code = " ".join(code.split())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
@@ -570,7 +572,7 @@ def bench_stamps(args):
     NS, NK = 16, per // 16
     nch = min((l + chunk - 1) // chunk for l in spec.seq_lens)
     c0 = max(0, nch // 2 - NS // 2)
-    buf = torch.zeros(3 * NS * NK, dtype=torch.int64, device=dev)
+    buf = torch.zeros(4 * NS * NK, dtype=torch.int64, device=dev)
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
     runs, scan_ms = [], []
     for rep in range(args.steps):
@@ -590,13 +592,13 @@ def bench_stamps(args):
         torch.cuda.synchronize()
         scan_ms.append(e0.elapsed_time(e1))
         if rep >= 1:  # the first call sets the kernels' launch attributes
-            runs.append(buf.cpu().numpy().reshape(3, NS, NK).astype(np.int64))
+            runs.append(buf.cpu().numpy().reshape(4, NS, NK).astype(np.int64))
     lib.gdn_debug_stamps(None, 0, 0)
     if int(status.item()):
         raise gdn.GdnStatusError(int(status.item()))
     a = np.stack(runs)  # [reps, role, step, phase]
     med = lambda x: float(np.median(x))
-    chain, out, cpy = a[:, 0], a[:, 1], a[:, 2]
+    chain, out, cpy, chain1 = a[:, 0], a[:, 1], a[:, 2], a[:, 3]
     period = med(chain[:, 1:, 0] - chain[:, :-1, 0])
     step_us = float(np.median(scan_ms)) * 1e3 / nch
     rows = [("chain wave 0", [("Y = K H_in, X", chain[:, :-1, 1] - chain[:, :-1, 0]),
@@ -604,6 +606,11 @@ def bench_stamps(args):
                               ("state update, H_in of next", chain[:, :-1, 3] - chain[:, :-1, 2]),
                               ("T loads issued, wait", chain[:, :-1, 4] - chain[:, :-1, 3]),
                               ("barrier", chain[:, 1:, 0] - chain[:, :-1, 4])]),
+            ("chain wave 1", [("Y = K H_in, X", chain1[:, :-1, 1] - chain1[:, :-1, 0]),
+                              ("R = T X, R S", chain1[:, :-1, 2] - chain1[:, :-1, 1]),
+                              ("state update, H_in of next", chain1[:, :-1, 3] - chain1[:, :-1, 2]),
+                              ("T loads issued, wait", chain1[:, :-1, 4] - chain1[:, :-1, 3]),
+                              ("barrier", chain1[:, 1:, 0] - chain1[:, :-1, 4])]),
             ("output wave", [("loads, P R of previous chunk, stores", out[:, :-1, 1] - out[:, :-1, 0]),
                              ("Q H_in of this chunk", out[:, :-1, 2] - out[:, :-1, 1]),
                              ("wait for loads / stores", out[:, :-1, 3] - out[:, :-1, 2]),
@@ -617,16 +624,29 @@ def bench_stamps(args):
     lines = ["# scan step phases (shader-clock ticks, s_memtime) of workgroup %d, chunk steps %d..%d: %s"
              % (args.stamp_block, c0, c0 + NS - 1, workload_title(args.config)),
              "# command: " + cmd,
-             "# medians over %d steps x %d calls (cache-cold scan launches of the split composition)"
-             % (NS - 1, len(runs)),
+             "# medians over %d steps x %d calls (cache-cold scan launches of the split composition);"
+             " then the 10th / 90th percentiles, and the medians of even and odd chunk steps"
+             " (the chain's T register sets alternate by chunk parity)" % (NS - 1, len(runs)),
              "source_digest: %s" % source_digest("hybrid"),
              "step_ticks: %.0f" % period,
              "step_us: %.3f  (scan kernel %.4f ms / %d chunk steps)" % (step_us, float(np.median(scan_ms)), nch),
              "ticks_per_us: %.0f" % (period / step_us)]
+    # chunk index of each step column of a phase array (steps c0 .. c0 + NS - 2)
+    even = ((c0 + np.arange(NS - 1)) % 2) == 0
+    pct = lambda x, q: float(np.percentile(x, q))
+    lines.append("%-42s %7s %7s %7s %7s %7s" % ("", "median", "p10", "p90", "even", "odd"))
+    per = chain[:, 1:, 0] - chain[:, :-1, 0]
+    lines.append("%-42s %7.0f %7.0f %7.0f %7.0f %7.0f" % ("step period (chain wave 0)", med(per), pct(per, 10),
+                                                           pct(per, 90), med(per[:, even]), med(per[:, ~even])))
     for role, phases in rows:
         lines.append("%s:" % role)
         for name, d in phases:
-            lines.append("  %-40s %7.0f" % (name, med(d)))
+            lines.append("  %-40s %7.0f %7.0f %7.0f %7.0f %7.0f" % (name, med(d), pct(d, 10), pct(d, 90),
+                                                                   med(d[:, even]), med(d[:, ~even])))
+    # histogram of the step period, 200-tick bins
+    lo = int(per.min()) // 200 * 200
+    hist = np.bincount(((per - lo) // 200).astype(np.int64).ravel())
+    lines.append("step period histogram (200-tick bins from %d): %s" % (lo, " ".join(str(int(h)) for h in hist)))
     txt = "\n".join(lines) + "\n"
     out = args.stamps_out or os.path.join(ROOT, "profiles", "scan_stamps_%s.txt" % args.config)
     os.makedirs(os.path.dirname(out), exist_ok=True)
@@ -962,6 +982,10 @@ def main():
         rec["copy_probe_bytes"] = copy_probe(args.copy_probe, dev)
     if args.peaks:
         rec["measured_peaks"] = measured_peaks(dev)
+        # the same achieved rate against the copy rate measured on this machine
+        rec["roofline"]["frac_of_measured_copy"] = achieved_gbs / rec["measured_peaks"]["hbm_copy_GBps"]
+        rec["mfma"]["layer_frac_of_measured_gemm"] = (flops / (ms_step * 1e-3) / 1e12
+                                                       / rec["measured_peaks"]["bf16_gemm_8192_TFLOPs"])
     if not args.no_cpu:
         log("timing the oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -431,8 +431,9 @@ int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 #ifdef GDN_SCAN_STAMPS
 // Measurement build only (not part of the ABI in include/gdn.h): the following calls' scan
 // workgroup `block` records, for kStampSteps chunk steps from chunk `c0`, a shader-clock
-// timestamp at each phase boundary of its chain wave 0, output wave and loader wave into
-// the device buffer `buf` ([3][kStampSteps][kStampPhases] uint64; NULL stops recording).
+// timestamp at each phase boundary of its chain wave 0, output wave, loader wave and chain
+// wave 1 into the device buffer `buf` ([4][kStampSteps][kStampPhases] uint64; NULL stops
+// recording).
 int32_t gdn_debug_stamps(void* buf, int32_t block, int32_t c0) {
   gdn::g_stamps = (uint64_t*)buf;
   gdn::g_stamp_block = block;

@@ -108,7 +108,7 @@ struct Params {
   float* Mws;
   float* Hws;
   // Step timestamps of one scan workgroup, recorded only by a library built with
-  // GDN_SCAN_STAMPS (a measurement build): [3 roles: chain wave 0, output, loader]
+  // GDN_SCAN_STAMPS (a measurement build): [4 roles: chain wave 0, output, loader, chain wave 1]
   // [kStampSteps steps from chunk stamp_c0][kStampPhases] shader-clock counts.
   uint64_t* stamps;
   int32_t stamp_block, stamp_c0;

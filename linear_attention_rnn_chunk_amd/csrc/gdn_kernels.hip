@@ -2037,7 +2037,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
       const unsigned char* B = bufp(ci);
       const float* S = scal(ci);
       const int par = ci & 1;
-      if (u == 0) GDN_STAMP(0, ci, 0);
+      GDN_STAMP(u == 0 ? 0 : 3, ci, 0);
       if (!PRE) load_kf(ci);
       // operands of the rest of this chunk, read (after K) while the products run
       float vv[NCT][NT][4];
@@ -2123,7 +2123,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
 #pragma unroll
         for (int sb = 0; sb < NBC; ++sb) XB[c][sb] = Arm::acc(X[2 * sb], X[2 * sb + 1]);
       }
-      if (u == 0) GDN_STAMP(0, ci, 1);  // Y = K H_in ready (X formed from it)
+      GDN_STAMP(u == 0 ? 0 : 3, ci, 1);  // Y = K H_in ready (X formed from it)
       // R = T X
       f32x4 R[NCT][NT];
 #pragma unroll
@@ -2161,7 +2161,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           }
         }
       }
-      if (u == 0) GDN_STAMP(0, ci, 2);  // R = T X ready (R stored, R S formed)
+      GDN_STAMP(u == 0 ? 0 : 3, ci, 2);  // R = T X ready (R stored, R S formed)
       // H <- e^{G_C} H_in + Ktil^T R
 #pragma unroll
       for (int sb = 0; sb < NBC; ++sb)
@@ -2177,7 +2177,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           HB[c][kb] = Arm::acc(H[c][2 * kb], H[c][2 * kb + 1]);
           Arm::stf(hb_at(par ^ 1, u, c, kb), HB[c][kb]);
         }
-      if (u == 0) GDN_STAMP(0, ci, 3);  // state update ready (H_in of the next chunk formed)
+      GDN_STAMP(u == 0 ? 0 : 3, ci, 3);  // state update ready (H_in of the next chunk formed)
       // chunk ci + 2's T into this chunk's set; chunk ci + 1's (issued a step ago) must be
       // complete at the barrier, chunk ci + 2's may stay in flight.  (The compiler also
       // waits for the newest set before R = T X in the first step of each pair, since it
@@ -2193,7 +2193,7 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           wait_vm<0>();
         }
       }
-      if (u == 0) GDN_STAMP(0, ci, 4);
+      GDN_STAMP(u == 0 ? 0 : 3, ci, 4);
       __syncthreads();
     };
     // whole pairs of steps, then a last odd step (no step skipped inside the loop body)
