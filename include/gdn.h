@@ -21,7 +21,9 @@
  *
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers owned by the caller; the library
- *     allocates and frees nothing and keeps no global state.
+ *     allocates and frees nothing per call.  Its only state is set once per device and
+ *     changes no result: which kernels have had their LDS size set, and the device
+ *     address of gdn_chunk_fwd_noalloc's workspace array.
  *   - Tensors are dense, row-major, last dimension contiguous, no padding.
  *   - Host-detected errors return synchronously and launch nothing.
  *   - gdn_chunk_fwd and gdn_decode_step are asynchronous on `stream`; device-detected
@@ -129,7 +131,9 @@ typedef struct gdn_problem {
  * explicit, section "Remaining work").
  *   p  the problem; read only
  * Returns GDN_OK, GDN_E_NULL (p is NULL), GDN_E_SHAPE (negative or inconsistent sizes,
- * tokens with no sequence) or GDN_E_UNSUPPORTED (outside the domain). */
+ * tokens with no sequence) or GDN_E_UNSUPPORTED (outside the domain, including a
+ * solve_block other than 0, 8, 16 or 32, and a solve_block other than 16 requested with
+ * the fused or pipelined composition, whose in-scan tile stages solve with 16 rows). */
 gdn_status gdn_validate(const gdn_problem* p);
 
 /* gdn_workspace_bytes -- bytes of device workspace gdn_chunk_fwd needs for *p, written to

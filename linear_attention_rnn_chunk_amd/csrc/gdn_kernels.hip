@@ -15,13 +15,18 @@
 // (per key channel for the per-channel gate, where the exp factors sit inside
 // the contractions).  Kernels:
 //   gdn_chunk_table  one block: sanitised cu_seqlens bounds + per-sequence chunk prefix
-//   gdn_prep         one workgroup per (chunk, key head) [per value head for the
-//                    per-channel gate]; fully sequence-parallel: gate sweep, K K^T
-//                    and Q K^T on MFMA, blocked unit-lower-triangular solve; writes
-//                    T and P for every value head of the group
-//   gdn_scan         one workgroup per (sequence, value head, 32 state columns), one
-//                    wave per 16 columns; fp32 state lives in MFMA accumulators and
-//                    never leaves registers; walks the chunks serially.  It also runs
+//   gdn_prep_head    per-head gate: one workgroup per (chunk, key head), one wave per
+//                    value head of the group; fully sequence-parallel: gate sweep, K K^T
+//                    and Q K^T on MFMA, blocked unit-lower-triangular solve (diagonal
+//                    blocks of 8, 16 or 32 rows); writes T and P of each value head
+//   gdn_prep_chan    per-key-channel gate: one workgroup per (chunk, value head); also
+//                    writes the gated operands e^G K, e^{G_C-G} K, e^G Q and e^{G_C}
+//   gdn_scan         one workgroup per (sequence, value head, 32 or 64 state columns),
+//                    chain waves of 16 or 32 columns; fp32 state lives in MFMA
+//                    accumulators and never leaves registers; walks the chunks
+//                    serially.  Raw inputs (row norms, beta and g formed from their raw
+//                    values) fold into the prep's tiles and the scan's per-row
+//                    scalars; nothing extra is materialised.  It also runs
 //                    any chunk range of each sequence from and to given state buffers
 //                    (the pipelined composition's segments, whose launches run the next
 //                    segment's prep in workgroups after the scan's own) and the parts of
