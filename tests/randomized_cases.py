@@ -1,5 +1,6 @@
 """Seeded random problems over the library's supported domain, for the randomized parity
-test (tests/test_gpu_randomized.py) and its host-side check (tests/test_randomized_cpu.py).
+test (tests/test_gpu_randomized.py) and its host-side check (tests/test_randomized_cpu.py);
+and seeded one-token steps for gdn_decode_step.
 
 Each case draws, from its own seed: the gate form and law, chunk, key/value widths, key
 heads and grouping, a fixed-length batch or a packed batch (empty, one-token and ragged
@@ -69,3 +70,32 @@ def draw(i: int) -> Case:
 
 
 CASES = [draw(i) for i in range(N_CASES)]
+
+
+# one-token steps (gdn_decode_step): sequences of one token each, from a drawn state or zero
+N_DECODE = 64
+
+
+@dataclass(frozen=True)
+class DecodeCase:
+    spec: inputs.Spec
+    o_dtype: str
+
+
+def draw_decode(i: int) -> DecodeCase:
+    r = np.random.default_rng(9000 + i)
+    gate = str(r.choice(["head", "channel"]))
+    law = str(r.choice(["uniform5", "uniform05"])) if gate == "channel" else str(r.choice(["clip5", "half", "full", "zero"]))
+    hk = int(r.choice([1, 2, 4]))
+    hv = hk * int(r.choice([1, 2, 3, 4]))
+    dk, dv = int(r.choice([32, 64, 128])), int(r.choice([32, 64, 128]))
+    B = int(r.choice([1, 2, 5, 17, 40]))
+    qkv = str(r.choice(["bf16", "f32"]))
+    o_dtype = "f32" if qkv == "f32" else str(r.choice(["bf16", "f32"]))
+    spec = inputs.Spec("step%d" % i, (1,) * B, hk, hv, dk, dv, qkv_dtype=qkv, gate=gate, gate_law=law,
+                       h0=bool(r.integers(4)), packed=True, seed=9500 + i,
+                       beta_law=str(r.choice(["sigmoid", "sigmoid", "one", "zero", "eps"])))
+    return DecodeCase(spec, o_dtype)
+
+
+DECODE_CASES = [draw_decode(i) for i in range(N_DECODE)]

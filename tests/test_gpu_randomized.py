@@ -12,7 +12,7 @@ import torch
 from oracle import prepare
 from linear_attention_rnn_chunk_amd import gdn, inputs
 from tests.gpu_util import BOUND, device_inputs, oracle_ref, rel, to_np64
-from tests.randomized_cases import CASES
+from tests.randomized_cases import CASES, DECODE_CASES
 
 pytestmark = pytest.mark.gpu
 
@@ -48,3 +48,30 @@ def test_randomized_case(i):
     eo, eh = rel(to_np64(o), o_ref), rel(to_np64(hT), h_ref)
     print("case %d rel-L2 o=%.3e hT=%.3e (bound %.0e)" % (i, eo, eh, BOUND[c.arm]), flush=True)
     assert eo <= BOUND[c.arm] and eh <= BOUND[c.arm], (eo, eh)
+
+
+# one-token steps: fp32 throughout, so h_out and an fp32 o within 1e-5, a bf16 o within 4e-3
+# (its own rounding, at most 2^-9 per element), as in tests/test_gpu_decode.py
+STEP_BOUND = {"h": 1e-5, "f32": 1e-5, "bf16": 4e-3}
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_CASES)))
+def test_randomized_step(i):
+    c = DECODE_CASES[i]
+    s = c.spec
+    print("step case %d: B=%d hk=%d hv=%d dk=%d dv=%d gate=%s/%s qkv=%s o=%s beta=%s h0=%s"
+          % (i, s.n_seq, s.hk, s.hv, s.dk, s.dv, s.gate, s.gate_law, s.qkv_dtype, c.o_dtype, s.beta_law, s.h0),
+          flush=True)
+    inp = inputs.make(s)
+    d = device_inputs(inp)
+    sq = lambda x: x.squeeze(0)
+    h_in = d["h0"]
+    h_keep = None if h_in is None else h_in.clone()
+    o, h_out, _ = gdn.decode_step(sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["g"]), sq(d["beta"]), h_in,
+                                  o_dtype=ODT[c.o_dtype])
+    o_ref, h_ref = oracle_ref(inp)
+    eo, eh = rel(to_np64(o), o_ref.reshape(o.shape)), rel(to_np64(h_out), h_ref)
+    print("step case %d rel-L2 o=%.3e h=%.3e" % (i, eo, eh), flush=True)
+    assert eo <= STEP_BOUND[c.o_dtype] and eh <= STEP_BOUND["h"], (eo, eh)
+    if h_keep is not None:
+        assert torch.equal(h_in, h_keep)  # the input state is never written

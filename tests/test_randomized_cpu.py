@@ -40,3 +40,10 @@ def test_the_mix_covers_the_domain():
     assert got(lambda c: c.spec.beta_law) == {"sigmoid", "one", "zero", "eps"}
     assert got(lambda c: c.spec.packed) == {True, False}
     assert any(0 in c.spec.seq_lens for c in rc.CASES) and any(1 in c.spec.seq_lens for c in rc.CASES)
+
+
+def test_step_draw_is_reproducible_and_covers_both_gates():
+    assert [rc.draw_decode(i) for i in range(rc.N_DECODE)] == rc.DECODE_CASES
+    assert {c.spec.gate for c in rc.DECODE_CASES} == {"head", "channel"}
+    assert {c.spec.h0 for c in rc.DECODE_CASES} == {True, False}
+    assert {c.o_dtype for c in rc.DECODE_CASES} == {"bf16", "f32"}
