@@ -1270,7 +1270,8 @@ __global__ __launch_bounds__(256) void gdn_prep_chan(Params p) {
 //               of NBUF chunk buffers, runs the in-chunk gate sweep ahead, checks V
 // One workgroup barrier per chunk.  The fused composition adds two tile waves that form T
 // and P in the workgroup (described with their code below).  In a pipelined launch the
-// workgroups past the scan's (blockIdx >= nscan) are prep workgroups (prep_role).
+// workgroups past the scan's (blockIdx >= nscan) are prep workgroups (prep_role); only the
+// PIPE instance carries that code.
 //
 // State rows are stored permuted within each 32-key block: accumulator tile t = 2 kb + h,
 // row 4 g + j holds key dim pi = 32 kb + 8 g + 4 h + j.  Two stacked accumulator tiles are
@@ -1499,7 +1500,7 @@ struct ScanLds {
   } while (0)
 #endif
 
-template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED, int NCT = 1>
+template <class Arm, int DK, int C, bool KDA, bool QF32, bool FUSED, int NCT = 1, bool PIPE = false>
 __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   using T = typename Arm::T;
   using F = typename Arm::F;
@@ -1507,7 +1508,11 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
   using SL = ScanLds<Arm, DK, C, KDA, QF32, FUSED, NCT>;
   constexpr int WC = SL::WC;  // state columns of this workgroup
   static_assert(!FUSED || (!KDA && !QF32), "fused composition: per-head gate, bf16 inputs");
-  if constexpr (!KDA && !FUSED) {
+  // PIPE: the kernel of pipelined launches, whose workgroups past the scan's run the next
+  // segment's prep.  Other launches use the instance without that code, which leaves the
+  // scan's own roles more registers.
+  if constexpr (PIPE) {
+    static_assert(!KDA && !FUSED, "prep workgroups: per-head gate, split layout");
     if ((int)blockIdx.x >= p.nscan) {  // pipelined composition: the next segment's prep
       prep_role<Arm, DK, C, QF32>(p);
       return;
@@ -2309,10 +2314,11 @@ __global__ __launch_bounds__(256) void gdn_seq_chain(Params p, int DK, int q) {
 }
 
 // ------------------------------------------------------------ launch -----
-// Kernel attributes are set once per instantiation and device (the first launch there);
-// later launches reuse them.
-template <class Fn>
-bool set_lds_once(Fn fn, size_t lds) {
+// Kernel attributes are set once per kernel and device (the first launch there); later
+// launches reuse them.  The kernel is a template argument, so each one has its own flags
+// (every kernel here has the same type, so a flag per type would be shared by all).
+template <auto Fn>
+bool set_lds_once(size_t lds) {
   // one flag per device (the attribute belongs to the function on the current device);
   // concurrent first calls may both set it, which is harmless
   static std::atomic<uint64_t> done{0};
@@ -2320,7 +2326,7 @@ bool set_lds_once(Fn fn, size_t lds) {
   if (hipGetDevice(&dev) != hipSuccess) return false;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (bit && (done.load(std::memory_order_acquire) & bit)) return true;
-  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+  if (hipFuncSetAttribute((const void*)Fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return false;
   done.fetch_or(bit, std::memory_order_release);
   return true;
@@ -2358,9 +2364,9 @@ gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int np
   const int S = (cps + SEG - 1) / SEG;
   auto cut = [&](int s) { return s < S ? s * SEG : cps; };
   const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
-  if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
+  if (!set_lds_once<gdn_prep_head<Arm, DK, C, QF32>>(4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
   using SL = ScanLds<Arm, DK, C, false, QF32, false, NCT>;
-  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false, NCT>, SL::BYTES)) return GDN_E_LAUNCH;
+  if (!set_lds_once<gdn_scan<Arm, DK, C, false, QF32, false, NCT, true>>(SL::BYTES)) return GDN_E_LAUNCH;
   Params q = prm;
   q.tile_ring = pl.tile_ring;  // (the plan's ring half is one segment, SEG chunks)
   q.prep_cb = 0;
@@ -2381,7 +2387,7 @@ gdn_status run_pipelined(const Plan& pl, const Params& prm, float* carry, int np
     q.h0_input = s == 0;
     q.hT = last ? prm.hT : carry;
     const int grid = q.nscan + (last ? 0 : nprep);
-    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false, NCT>), dim3((unsigned)grid), dim3(256), SL::BYTES,
+    hipLaunchKernelGGL((gdn_scan<Arm, DK, C, false, QF32, false, NCT, true>), dim3((unsigned)grid), dim3(256), SL::BYTES,
                        st, q);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
@@ -2428,9 +2434,9 @@ int seqsplit_parts(const Plan& pl, int nscan) {
 template <class Arm, int DK, int C, bool QF32, int NCT>
 gdn_status run_seqsplit(const Plan& pl, const Params& prm, int parts, hipStream_t st) {
   const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
-  if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
+  if (!set_lds_once<gdn_prep_head<Arm, DK, C, QF32>>(4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
   using SL = ScanLds<Arm, DK, C, false, QF32, false, NCT>;
-  if (!set_lds_once(gdn_scan<Arm, DK, C, false, QF32, false, NCT>, SL::BYTES)) return GDN_E_LAUNCH;
+  if (!set_lds_once<gdn_scan<Arm, DK, C, false, QF32, false, NCT>>(SL::BYTES)) return GDN_E_LAUNCH;
   hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)((pl.max_slots + 7) / 8 * 8 * pl.hk * nblk)),
                      dim3(64 * wpb), wpb * SolveLds<C>::FLOATS * sizeof(float), st, prm);
   if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
@@ -2473,13 +2479,13 @@ gdn_status run_cols(const Plan& pl, const Params& prm0, void* carry, hipStream_t
   if (pl.run_prep && !pl.fused && pl.max_slots > 0) {
     if constexpr (KDA) {
       const size_t lds = prep_chan_lds_bytes<Arm, DK>();
-      if (!set_lds_once(gdn_prep_chan<Arm, DK, QF32>, lds)) return GDN_E_LAUNCH;
+      if (!set_lds_once<gdn_prep_chan<Arm, DK, QF32>>(lds)) return GDN_E_LAUNCH;
       const int64_t blocks = pl.max_slots * pl.hv;
       hipLaunchKernelGGL((gdn_prep_chan<Arm, DK, QF32>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     } else {
       const int group = pl.hv / pl.hk, wpb = group < 4 ? group : 4, nblk = (group + wpb - 1) / wpb;
       const size_t lds = wpb * SolveLds<C>::FLOATS * sizeof(float);
-      if (!set_lds_once(gdn_prep_head<Arm, DK, C, QF32>, 4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
+      if (!set_lds_once<gdn_prep_head<Arm, DK, C, QF32>>(4 * SolveLds<C>::FLOATS * sizeof(float))) return GDN_E_LAUNCH;
       const int64_t blocks = (pl.max_slots + 7) / 8 * 8 * pl.hk * nblk;  // whole groups of 8 slots
       hipLaunchKernelGGL((gdn_prep_head<Arm, DK, C, QF32>), dim3((unsigned)blocks), dim3(64 * wpb), lds, st, prm);
     }
@@ -2490,14 +2496,14 @@ gdn_status run_cols(const Plan& pl, const Params& prm0, void* carry, hipStream_t
     if constexpr (!KDA && !QF32 && NCT == 1 && std::is_same<Arm, ArmBF16>::value) {
       if (pl.fused) {
         const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, true>::BYTES;
-        if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, true>, lds)) return GDN_E_LAUNCH;
+        if (!set_lds_once<gdn_scan<Arm, DK, C, KDA, QF32, true>>(lds)) return GDN_E_LAUNCH;
         hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32, true>), dim3((unsigned)blocks), dim3(384), lds, st, prm);
         return hipGetLastError() == hipSuccess ? GDN_OK : GDN_E_LAUNCH;
       }
     }
     if (pl.fused) return GDN_E_UNSUPPORTED;  // refused on the host already
     const size_t lds = ScanLds<Arm, DK, C, KDA, QF32, false, NCT>::BYTES;
-    if (!set_lds_once(gdn_scan<Arm, DK, C, KDA, QF32, false, NCT>, lds)) return GDN_E_LAUNCH;
+    if (!set_lds_once<gdn_scan<Arm, DK, C, KDA, QF32, false, NCT>>(lds)) return GDN_E_LAUNCH;
     hipLaunchKernelGGL((gdn_scan<Arm, DK, C, KDA, QF32, false, NCT>), dim3((unsigned)blocks), dim3(256), lds, st, prm);
     if (hipGetLastError() != hipSuccess) return GDN_E_LAUNCH;
   }
