@@ -73,3 +73,17 @@ def test_library_input_side_by_hand(i):
     o, hT, _ = gdn.chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], chunk=64, arm="f32",
                              o_dtype=torch.float32, raw=(e["q_scale"], e["gate_scale"]))
     _check(e, o, hT, dk, dv)
+
+
+ONE_TOKEN = [i for i, e in enumerate(EX) if all(b - a == 1 for a, b in zip(e["seq_start"], e["seq_start"][1:]))]
+
+
+@pytest.mark.parametrize("i", ONE_TOKEN, ids=["ex%d" % i for i in ONE_TOKEN])
+def test_decode_step_by_hand(i):
+    """The one-token step (gdn_decode_step) on the examples whose sequences are one token
+    each: the batch is the examples' tokens, each continuing from its own state."""
+    e = EX[i]
+    a, _, dk, dv = _padded(e)
+    o, h_out, _ = gdn.decode_step(a["q"][0].contiguous(), a["k"][0].contiguous(), a["v"][0].contiguous(),
+                                  a["g"][0].contiguous(), a["beta"][0].contiguous(), a["h0"], o_dtype=torch.float32)
+    _check(e, o, h_out, dk, dv)
