@@ -57,17 +57,26 @@ def oracle_ref(inp, units=None, want_o=True, mutant=oracle.CORRECT):
                              units=units, want_o=want_o, mutant=mutant)
 
 
+# fp32's grid below 2^-126 (its subnormals) has the fixed spacing 2^-149, so there a value
+# is held to an absolute, not a relative, resolution: a state decayed into that band by
+# e^-90 .. e^-103 carries an error of a grid step or so from its last few fp32 roundings
+# however exactly it was computed.  Each element's error counts only beyond 16 such steps;
+# against a normal fp32 value (>= 2^-126) that allowance is at most 2^-19 of the value.
+SUBNORMAL_ALLOWANCE = 16 * 2.0 ** -149
+
+
 def rel(x, ref):
     """NaN-aware relative L2 of a GPU result x against the fp64 oracle's ref.  ref is first
     taken to fp32 (the exponent range of every output, fp32 or bf16): a value below that
     range (a state decayed by e^-160, say) has no representation but zero there, so it
-    cannot count as error."""
+    cannot count as error; and each element's error counts beyond SUBNORMAL_ALLOWANCE."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64).astype(np.float32).astype(np.float64)
     if not np.all(np.isfinite(x)):
         return float("inf")
+    err = np.maximum(np.abs(x - ref) - SUBNORMAL_ALLOWANCE, 0.0)
     den = np.linalg.norm(ref.ravel())
-    return float(np.linalg.norm((x - ref).ravel()) / den) if den > 0 else float(np.linalg.norm(x.ravel()))
+    return float(np.linalg.norm(err.ravel()) / den) if den > 0 else float(np.linalg.norm(err.ravel()))
 
 
 def oracle_units(inp, units, want_o=True):
