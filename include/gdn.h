@@ -169,7 +169,11 @@ gdn_status gdn_plan_compose(const gdn_problem* p, int32_t* compose);
  * state; "Verified implementation boundary": sticky numerical status).
  *   q, k        [total_tokens][hk][dk]   qkv_dtype, 16-byte aligned
  *   v           [total_tokens][hv][dv]   qkv_dtype, 16-byte aligned
- *   g           fp32 natural-log decay, [total_tokens][hv] or [total_tokens][hv][dk]
+ *   g           fp32 natural-log decay, [total_tokens][hv] or [total_tokens][hv][dk];
+ *               a per-head gate has no lower limit: at or below -200 a token resets the
+ *               state (every decay across it is below fp32's resolution and is taken as
+ *               exactly zero), and the in-chunk sums are formed in fp64, so the arm's
+ *               accuracy holds however large the gates
  *   beta        fp32 [total_tokens][hv]
  *   h0          fp32 [n_seq][hv][dk][dv] initial states, or NULL for zeros; never written
  *   cu_seqlens  int32 [n_seq+1] token offsets (0, ..., total_tokens), or NULL for a

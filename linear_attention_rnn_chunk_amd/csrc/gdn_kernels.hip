@@ -13,7 +13,9 @@
 //   Ktil_s = k_s * exp(G_C - G_s)
 //
 // (per key channel for the per-channel gate, where the exp factors sit inside
-// the contractions).  Kernels:
+// the contractions).  Under the per-head gate every factor comes from an fp64 in-chunk
+// prefix that restarts after a reset token (gate at most -200) and is zero across one
+// (gate_prefix).  Kernels:
 //   gdn_chunk_table  one block: sanitised cu_seqlens bounds + per-sequence chunk prefix
 //   gdn_prep_head    per-head gate: one workgroup per (chunk, key head), one wave per
 //                    value head of the group; fully sequence-parallel: gate sweep, K K^T
@@ -125,32 +127,49 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
   return __builtin_bit_cast(uint2, b);
 }
 
-__device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-// Inclusive prefix sum over the 64 lanes with DPP lane moves (no LDS round trips):
-// shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's (row 2's) last lane is
-// added to row 1 (row 3), then lane 31 to rows 2 and 3.  Lanes a move has no source for
-// add 0 (bound_ctrl), rows outside a move's row mask keep adding 0.
-__device__ __forceinline__ float wave_prefix_sum_dpp(float x) {
-  auto mv = [](float v, auto CTRL, auto ROWS) __attribute__((always_inline)) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(CTRL)::value,
-                                                      decltype(ROWS)::value, 0xf, true));
-  };
+// The per-head gate's in-chunk prefix, lane = token, for the factors e^{G_r - G_s} of the
+// tiles and e^{G}, e^{G_C - G}, e^{G_C} of the scan.  Two things keep those exact to fp32
+// however large the chunk's gates:
+//  - A token whose gate is at most kResetGate is a reset: e^{-200} times any finite fp32
+//    operand is below half of fp32's smallest subnormal, so every factor across such a
+//    token is exactly zero.  The prefix restarts after it.
+//  - The prefix is summed in fp64, so a chunk whose gates add up to thousands still gives
+//    the small difference of two of its sums exactly (an fp32 prefix of -1e4 has a grid
+//    of 1e-3).
+// Returns s = the gate summed over the tokens after the last reset up to this one (0 at a
+// reset), and n = the resets up to this one.  For r >= s the factor is then
+// e^{G_r - G_s} = (n_r != n_s) ? 0 : e^{s_r - s_s}, and e^{G_r} = n_r ? 0 : e^{s_r}.
+// Segmented inclusive scan over the 64 lanes with DPP lane moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's (row 2's) last lane into
+// row 1 (row 3), then lane 31 into rows 2 and 3.  A window's sum takes its left
+// neighbour's only when the window holds no reset; lanes a move has no source for, and
+// rows outside its row mask, receive (0, 0), which changes nothing.
+constexpr float kResetGate = -200.f;
+struct GatePrefix {
+  double s;
+  int n;
+};
+__device__ __forceinline__ GatePrefix gate_prefix(float x) {
   using std::integral_constant;
-  x += mv(x, integral_constant<int, 0x111>{}, integral_constant<int, 0xf>{});  // row_shr:1
-  x += mv(x, integral_constant<int, 0x112>{}, integral_constant<int, 0xf>{});  // row_shr:2
-  x += mv(x, integral_constant<int, 0x114>{}, integral_constant<int, 0xf>{});  // row_shr:4
-  x += mv(x, integral_constant<int, 0x118>{}, integral_constant<int, 0xf>{});  // row_shr:8
-  x += mv(x, integral_constant<int, 0x142>{}, integral_constant<int, 0xa>{});  // row_bcast:15
-  x += mv(x, integral_constant<int, 0x143>{}, integral_constant<int, 0xc>{});  // row_bcast:31
-  return x;
+  auto mv = [](int v, auto CTRL, auto ROWS) __attribute__((always_inline)) {
+    return __builtin_amdgcn_update_dpp(0, v, decltype(CTRL)::value, decltype(ROWS)::value, 0xf, true);
+  };
+  const int reset = x <= kResetGate;
+  double s = reset ? 0.0 : (double)x;
+  int n = reset;
+  auto step = [&](auto CTRL, auto ROWS) __attribute__((always_inline)) {
+    const int lo = mv(__double2loint(s), CTRL, ROWS), hi = mv(__double2hiint(s), CTRL, ROWS);
+    const int nl = mv(n, CTRL, ROWS);
+    if (n == 0) s = __hiloint2double(hi, lo) + s;  // lanes without a source add +0
+    n += nl;
+  };
+  step(integral_constant<int, 0x111>{}, integral_constant<int, 0xf>{});  // row_shr:1
+  step(integral_constant<int, 0x112>{}, integral_constant<int, 0xf>{});  // row_shr:2
+  step(integral_constant<int, 0x114>{}, integral_constant<int, 0xf>{});  // row_shr:4
+  step(integral_constant<int, 0x118>{}, integral_constant<int, 0xf>{});  // row_shr:8
+  step(integral_constant<int, 0x142>{}, integral_constant<int, 0xa>{});  // row_bcast:15
+  step(integral_constant<int, 0x143>{}, integral_constant<int, 0xc>{});  // row_bcast:31
+  return {s, n};
 }
 
 // ---------------------------------------------------------------- arms ----
@@ -462,9 +481,11 @@ __host__ __device__ constexpr int tri(int rt, int st) { return rt * (rt + 1) / 2
 template <int C>
 struct SolveLds {
   static constexpr int NT = C / 16, NTRI = NT * (NT + 1) / 2;
-  // the lower tiles, then the chunk's G and beta rows and (raw inputs) 1 / |k_r| and
-  // q_scale / |q_r|
-  static constexpr int FLOATS = NTRI * kTile + 4 * C;
+  // the lower tiles, then the chunk's G and beta rows, (raw inputs) 1 / |k_r| and
+  // q_scale / |q_r|, and G's low-order part and reset count (gate_prefix: G = hi + lo in
+  // two floats, the count as int bits), at G_LO and G_N past G's row
+  static constexpr int FLOATS = NTRI * kTile + 6 * C;
+  static constexpr int G_LO = 4 * C, G_N = 5 * C;
 };
 
 // One wave's LDS accesses in program order, complete: data some lanes wrote is then
@@ -646,23 +667,35 @@ __device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, c
   wave_lds_sync();  // G and beta rows (and row norms) written by other lanes
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    const float Gr = KDA ? 0.f : Gs[16 * rt + i];
+    constexpr int GL = SolveLds<C>::G_LO, GN = SolveLds<C>::G_N;
+    const float Gr = KDA ? 0.f : Gs[16 * rt + i], Glr = KDA ? 0.f : Gs[GL + 16 * rt + i];
+    const int nr = KDA ? 0 : __float_as_int(Gs[GN + 16 * rt + i]);
     const float nkr = Nk ? Nk[16 * rt + i] : 1.f, nqr = Nk ? Nq[16 * rt + i] : 1.f;
     const float br = Bs[16 * rt + i] * nkr;  // zero for rows past the chunk end
     const bool live = 16 * rt + i < L;
 #pragma unroll
     for (int st = 0; st <= rt; ++st) {
       const int t = tri(rt, st);
-      float4 G4 = {0.f, 0.f, 0.f, 0.f}, N4 = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (!KDA) G4 = *(const float4*)(Gs + 16 * st + 4 * g);
+      float4 G4 = {0.f, 0.f, 0.f, 0.f}, L4 = {0.f, 0.f, 0.f, 0.f}, N4 = {1.f, 1.f, 1.f, 1.f};
+      int4 R4 = {0, 0, 0, 0};
+      if constexpr (!KDA) {
+        G4 = *(const float4*)(Gs + 16 * st + 4 * g);
+        L4 = *(const float4*)(Gs + GL + 16 * st + 4 * g);
+        R4 = *(const int4*)(Gs + GN + 16 * st + 4 * g);
+      }
       if (Nk) N4 = *(const float4*)(Nk + 16 * st + 4 * g);
-      const float Gsv[4] = {G4.x, G4.y, G4.z, G4.w}, Nks[4] = {N4.x, N4.y, N4.z, N4.w};
+      const float Gsv[4] = {G4.x, G4.y, G4.z, G4.w}, Glv[4] = {L4.x, L4.y, L4.z, L4.w};
+      const float Nks[4] = {N4.x, N4.y, N4.z, N4.w};
+      const int nsv[4] = {R4.x, R4.y, R4.z, R4.w};
       f32x4 a, pv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool lower = st < rt || 4 * g + j < i;
         const bool ldiag = live && (st < rt || 4 * g + j <= i);
-        const float e = (KDA ? 1.f : nexp(Gr - Gsv[j])) * Nks[j];  // s > r entries are discarded
+        // e^{G_r - G_s}: zero across a reset; else the two-float difference, exact for
+        // nearby rows (s > r entries are discarded)
+        const float e =
+            (KDA ? 1.f : (nr != nsv[j] ? 0.f : nexp((Gr - Gsv[j]) + (Glr - Glv[j])))) * Nks[j];
         a[j] = lower ? br * (e * accA[t][j]) : 0.f;
         pv[j] = ldiag ? (e * accP[t][j]) * nqr : 0.f;
       }
@@ -845,8 +878,8 @@ __device__ __forceinline__ uint32_t tile_products_lean(const Params& p, int64_t 
   return flag_if(nf, GDN_ST_NONFINITE_INPUT);
 }
 
-// G (inclusive prefix of the gate) and beta of the chunk's rows into Gs, Bs (rows past
-// the end contribute gate 0 and beta 0); returns the status bits of the gate and beta
+// G (the gate's in-chunk prefix, gate_prefix) and beta of the chunk's rows into Gs, Bs
+// (rows past the end contribute gate 0 and beta 0); returns the status bits of the gate and beta
 // (raw inputs: xl and bl are the raw gate value and the beta logit, transformed here)
 template <int C>
 __device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int lane, float* Gs, float* Bs,
@@ -858,9 +891,12 @@ __device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int la
     b = sigmoid_f(b);
   }
   bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
-  const float G = wave_prefix_sum(x, lane);
+  const GatePrefix G = gate_prefix(x);
   if (lane < C) {
-    Gs[lane] = G;
+    const float hi = (float)G.s;
+    Gs[lane] = hi;
+    Gs[SolveLds<C>::G_LO + lane] = (float)(G.s - (double)hi);
+    Gs[SolveLds<C>::G_N + lane] = __int_as_float(G.n);
     Bs[lane] = b;
   }
   return bad;
@@ -1721,16 +1757,19 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           nq = ((const float*)(B + SL::NR + 4 * C))[lane < C ? lane : C - 1];
         }
         bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
-        const float G = wave_prefix_sum_dpp(x);
-        const float GC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
+        // e^{G}, e^{G_C - G} and e^{G_C} of the rows from gate_prefix: zero across a reset
+        const GatePrefix G = gate_prefix(x);
+        const double GC = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(G.s), C - 1),
+                                           __builtin_amdgcn_readlane(__double2loint(G.s), C - 1));
+        const int nC = __builtin_amdgcn_readlane(G.n, C - 1);
         if (lane < C) {
-          const float eg = nexp(G);
+          const float eg = G.n ? 0.f : nexp((float)G.s);
           S[lane] = b;
           S[C + lane] = b * eg * nk;
-          S[2 * C + lane] = nexp(GC - G) * nk;
+          S[2 * C + lane] = nC != G.n ? 0.f : nexp((float)(GC - G.s)) * nk;
           S[3 * C + lane] = eg * nq;
         }
-        if (lane == 0) S[4 * C] = nexp(GC);
+        if (lane == 0) S[4 * C] = nC ? 0.f : nexp((float)GC);
       } else {
         if (lane < C) S[lane] = b;
 #pragma unroll
