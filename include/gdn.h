@@ -100,7 +100,7 @@ enum { GDN_STAGE_ALL = 0, GDN_STAGE_PREP = 1, GDN_STAGE_SCAN = 2 };
 
 typedef struct gdn_problem {
   int32_t n_seq;        /* number of sequences, >= 0 */
-  int64_t total_tokens; /* packed token count, >= 0 */
+  int64_t total_tokens; /* packed token count, >= 0; with cu_seqlens at most 2^31 - 65 */
   int32_t seq_len;      /* fixed-length batches: tokens per sequence (total = n_seq*seq_len);
                            0 when cu_seqlens describes the sequences */
   int32_t hk;           /* key/query heads, >= 1 */

@@ -95,7 +95,9 @@ gdn_status make_plan(const gdn_problem* p, Plan* out, bool raw) {
   pl.varlen = !(p->seq_len > 0 || p->total_tokens == 0);
   const int64_t C = pl.chunk;
   if (pl.varlen) {
-    if (p->total_tokens > INT32_MAX) return GDN_E_UNSUPPORTED;  // int32 cu_seqlens
+    // int32 cu_seqlens, and the device rounds a sequence's length up to whole chunks in
+    // int32 (length + C - 1)
+    if (p->total_tokens > INT32_MAX - 64) return GDN_E_UNSUPPORTED;
     pl.chunks_per_seq = 0;
     pl.max_slots = (p->total_tokens + C - 1) / C + p->n_seq;
   } else {

@@ -58,6 +58,9 @@ def P(**kw):
     (dict(total_tokens=255), gdn.GDN_E_SHAPE),           # != n_seq * seq_len
     (dict(n_seq=0, seq_len=0), gdn.GDN_E_SHAPE),          # tokens that belong to no sequence
     (dict(n_seq=0, total_tokens=0, seq_len=0), gdn.GDN_OK),
+    # packed batches: int32 offsets, rounded up to whole chunks in int32 on the device
+    (dict(n_seq=3, seq_len=0, total_tokens=2**31 - 1 - 64, hk=1, hv=1, dk=32, dv=32), gdn.GDN_OK),
+    (dict(n_seq=3, seq_len=0, total_tokens=2**31 - 1 - 63, hk=1, hv=1, dk=32, dv=32), gdn.GDN_E_UNSUPPORTED),
     (dict(hv=5), gdn.GDN_E_UNSUPPORTED),                 # hv % hk
     (dict(dk=96), gdn.GDN_E_UNSUPPORTED),
     (dict(dv=256), gdn.GDN_E_UNSUPPORTED),
