@@ -14,8 +14,8 @@
 //
 // (per key channel for the per-channel gate, where the exp factors sit inside
 // the contractions).  Under the per-head gate every factor comes from an fp64 in-chunk
-// prefix that restarts after a reset token (gate at most -200) and is zero across one
-// (gate_prefix).  Kernels:
+// prefix in which a reset token (gate at most -200) counts as -2^20, so that every factor
+// across one is zero (gate_prefix).  Kernels:
 //   gdn_chunk_table  one block: sanitised cu_seqlens bounds + per-sequence chunk prefix
 //   gdn_prep_head    per-head gate: one workgroup per (chunk, key head), one wave per
 //                    value head of the group; fully sequence-parallel: gate sweep, K K^T
@@ -132,36 +132,27 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
 // however large the chunk's gates:
 //  - A token whose gate is at most kResetGate is a reset: e^{-200} times any finite fp32
 //    operand is below half of fp32's smallest subnormal, so every factor across such a
-//    token is exactly zero.  The prefix restarts after it.
+//    token is exactly zero.  Its gate enters the prefix as -2^20 (kResetSum), which makes
+//    every such factor e^{-2^20 + ...} = 0 and keeps the sums small enough for fp64 to
+//    add the other gates exactly (to about 1e-8 after 64 resets).
 //  - The prefix is summed in fp64, so a chunk whose gates add up to thousands still gives
 //    the small difference of two of its sums exactly (an fp32 prefix of -1e4 has a grid
 //    of 1e-3).
-// Returns s = the gate summed over the tokens after the last reset up to this one (0 at a
-// reset), and n = the resets up to this one.  For r >= s the factor is then
-// e^{G_r - G_s} = (n_r != n_s) ? 0 : e^{s_r - s_s}, and e^{G_r} = n_r ? 0 : e^{s_r}.
-// Segmented inclusive scan over the 64 lanes with DPP lane moves (no LDS round trips):
-// shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's (row 2's) last lane into
-// row 1 (row 3), then lane 31 into rows 2 and 3.  A window's sum takes its left
-// neighbour's only when the window holds no reset; lanes a move has no source for, and
-// rows outside its row mask, receive (0, 0), which changes nothing.
+// Inclusive prefix over the 64 lanes with DPP lane moves (no LDS round trips): shifts by
+// 1, 2, 4, 8 within each row of 16 lanes, then row 0's (row 2's) last lane is added to
+// row 1 (row 3), then lane 31 to rows 2 and 3.  Lanes a move has no source for add 0
+// (bound_ctrl), rows outside a move's row mask keep adding 0.
 constexpr float kResetGate = -200.f;
-struct GatePrefix {
-  double s;
-  int n;
-};
-__device__ __forceinline__ GatePrefix gate_prefix(float x) {
+constexpr double kResetSum = -1048576.0;
+__device__ __forceinline__ double gate_prefix(float x) {
   using std::integral_constant;
   auto mv = [](int v, auto CTRL, auto ROWS) __attribute__((always_inline)) {
     return __builtin_amdgcn_update_dpp(0, v, decltype(CTRL)::value, decltype(ROWS)::value, 0xf, true);
   };
-  const int reset = x <= kResetGate;
-  double s = reset ? 0.0 : (double)x;
-  int n = reset;
+  double s = x <= kResetGate ? kResetSum : (double)x;
   auto step = [&](auto CTRL, auto ROWS) __attribute__((always_inline)) {
     const int lo = mv(__double2loint(s), CTRL, ROWS), hi = mv(__double2hiint(s), CTRL, ROWS);
-    const int nl = mv(n, CTRL, ROWS);
-    if (n == 0) s = __hiloint2double(hi, lo) + s;  // lanes without a source add +0
-    n += nl;
+    s = __hiloint2double(hi, lo) + s;
   };
   step(integral_constant<int, 0x111>{}, integral_constant<int, 0xf>{});  // row_shr:1
   step(integral_constant<int, 0x112>{}, integral_constant<int, 0xf>{});  // row_shr:2
@@ -169,7 +160,7 @@ __device__ __forceinline__ GatePrefix gate_prefix(float x) {
   step(integral_constant<int, 0x118>{}, integral_constant<int, 0xf>{});  // row_shr:8
   step(integral_constant<int, 0x142>{}, integral_constant<int, 0xa>{});  // row_bcast:15
   step(integral_constant<int, 0x143>{}, integral_constant<int, 0xc>{});  // row_bcast:31
-  return {s, n};
+  return s;
 }
 
 // ---------------------------------------------------------------- arms ----
@@ -482,10 +473,10 @@ template <int C>
 struct SolveLds {
   static constexpr int NT = C / 16, NTRI = NT * (NT + 1) / 2;
   // the lower tiles, then the chunk's G and beta rows, (raw inputs) 1 / |k_r| and
-  // q_scale / |q_r|, and G's low-order part and reset count (gate_prefix: G = hi + lo in
-  // two floats, the count as int bits), at G_LO and G_N past G's row
-  static constexpr int FLOATS = NTRI * kTile + 6 * C;
-  static constexpr int G_LO = 4 * C, G_N = 5 * C;
+  // q_scale / |q_r|, and G's low-order part (gate_prefix: G = hi + lo in two floats) at
+  // G_LO past G's row
+  static constexpr int FLOATS = NTRI * kTile + 5 * C;
+  static constexpr int G_LO = 4 * C;
 };
 
 // One wave's LDS accesses in program order, complete: data some lanes wrote is then
@@ -667,9 +658,8 @@ __device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, c
   wave_lds_sync();  // G and beta rows (and row norms) written by other lanes
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    constexpr int GL = SolveLds<C>::G_LO, GN = SolveLds<C>::G_N;
+    constexpr int GL = SolveLds<C>::G_LO;
     const float Gr = KDA ? 0.f : Gs[16 * rt + i], Glr = KDA ? 0.f : Gs[GL + 16 * rt + i];
-    const int nr = KDA ? 0 : __float_as_int(Gs[GN + 16 * rt + i]);
     const float nkr = Nk ? Nk[16 * rt + i] : 1.f, nqr = Nk ? Nq[16 * rt + i] : 1.f;
     const float br = Bs[16 * rt + i] * nkr;  // zero for rows past the chunk end
     const bool live = 16 * rt + i < L;
@@ -677,25 +667,21 @@ __device__ __forceinline__ void wave_tiles(f32x4* accA, f32x4* accP, float* S, c
     for (int st = 0; st <= rt; ++st) {
       const int t = tri(rt, st);
       float4 G4 = {0.f, 0.f, 0.f, 0.f}, L4 = {0.f, 0.f, 0.f, 0.f}, N4 = {1.f, 1.f, 1.f, 1.f};
-      int4 R4 = {0, 0, 0, 0};
       if constexpr (!KDA) {
         G4 = *(const float4*)(Gs + 16 * st + 4 * g);
         L4 = *(const float4*)(Gs + GL + 16 * st + 4 * g);
-        R4 = *(const int4*)(Gs + GN + 16 * st + 4 * g);
       }
       if (Nk) N4 = *(const float4*)(Nk + 16 * st + 4 * g);
       const float Gsv[4] = {G4.x, G4.y, G4.z, G4.w}, Glv[4] = {L4.x, L4.y, L4.z, L4.w};
       const float Nks[4] = {N4.x, N4.y, N4.z, N4.w};
-      const int nsv[4] = {R4.x, R4.y, R4.z, R4.w};
       f32x4 a, pv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool lower = st < rt || 4 * g + j < i;
         const bool ldiag = live && (st < rt || 4 * g + j <= i);
-        // e^{G_r - G_s}: zero across a reset; else the two-float difference, exact for
-        // nearby rows (s > r entries are discarded)
-        const float e =
-            (KDA ? 1.f : (nr != nsv[j] ? 0.f : nexp((Gr - Gsv[j]) + (Glr - Glv[j])))) * Nks[j];
+        // e^{G_r - G_s} from the two-float difference, exact for nearby rows and zero
+        // across a reset (s > r entries are discarded)
+        const float e = (KDA ? 1.f : nexp((Gr - Gsv[j]) + (Glr - Glv[j]))) * Nks[j];
         a[j] = lower ? br * (e * accA[t][j]) : 0.f;
         pv[j] = ldiag ? (e * accP[t][j]) * nqr : 0.f;
       }
@@ -891,12 +877,11 @@ __device__ __forceinline__ uint32_t tile_sweep(float xl, float bl, int L, int la
     b = sigmoid_f(b);
   }
   bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
-  const GatePrefix G = gate_prefix(x);
+  const double G = gate_prefix(x);
   if (lane < C) {
-    const float hi = (float)G.s;
+    const float hi = (float)G;
     Gs[lane] = hi;
-    Gs[SolveLds<C>::G_LO + lane] = (float)(G.s - (double)hi);
-    Gs[SolveLds<C>::G_N + lane] = __int_as_float(G.n);
+    Gs[SolveLds<C>::G_LO + lane] = (float)(G - (double)hi);
     Bs[lane] = b;
   }
   return bad;
@@ -1757,19 +1742,18 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
           nq = ((const float*)(B + SL::NR + 4 * C))[lane < C ? lane : C - 1];
         }
         bad |= flag_if(x > 0.f, GDN_ST_GATE_DOMAIN);
-        // e^{G}, e^{G_C - G} and e^{G_C} of the rows from gate_prefix: zero across a reset
-        const GatePrefix G = gate_prefix(x);
-        const double GC = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(G.s), C - 1),
-                                           __builtin_amdgcn_readlane(__double2loint(G.s), C - 1));
-        const int nC = __builtin_amdgcn_readlane(G.n, C - 1);
+        // e^{G}, e^{G_C - G} and e^{G_C} of the rows from gate_prefix (zero across a reset)
+        const double G = gate_prefix(x);
+        const double GC = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(G), C - 1),
+                                           __builtin_amdgcn_readlane(__double2loint(G), C - 1));
         if (lane < C) {
-          const float eg = G.n ? 0.f : nexp((float)G.s);
+          const float eg = nexp((float)G);
           S[lane] = b;
           S[C + lane] = b * eg * nk;
-          S[2 * C + lane] = nC != G.n ? 0.f : nexp((float)(GC - G.s)) * nk;
+          S[2 * C + lane] = nexp((float)(GC - G)) * nk;
           S[3 * C + lane] = eg * nq;
         }
-        if (lane == 0) S[4 * C] = nC ? 0.f : nexp((float)GC);
+        if (lane == 0) S[4 * C] = nexp((float)GC);
       } else {
         if (lane < C) S[lane] = b;
 #pragma unroll

@@ -1,10 +1,11 @@
 """Per-head gates far below the usual range: reset tokens and chunks whose gates add up
-to thousands.  The in-chunk prefix is fp64 and restarts after a reset token (gate at
-most -200, where every factor across the token is below fp32's resolution and exactly
-zero), so every arm keeps its bound however large the gates; an fp32 prefix lost the
-fp32 arm's bound from gates of -1e4 on, and the bf16 arm's from -1e6 (its difference
-of two in-chunk sums then has a grid of 1e-3 and 0.06).  Both arms, every composition
-that applies, the raw-input entry point, against the fp64 oracle."""
+to thousands.  The in-chunk prefix is fp64, and a reset token (gate at most -200, where
+every factor across the token is below fp32's resolution) enters it as -2^20, so every
+factor across one is exactly zero and every arm keeps its bound however large the
+gates.  An fp32 prefix lost the fp32 arm's bound from gates of -1e4 on, and the bf16
+arm's from -1e6 (its difference of two in-chunk sums then has a grid of 1e-3 and 0.06).
+Both arms, every composition that applies, the raw-input entry point, against the fp64
+oracle."""
 import dataclasses
 
 import numpy as np
