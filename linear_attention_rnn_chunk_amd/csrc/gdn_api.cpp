@@ -119,7 +119,8 @@ gdn_status make_plan(const gdn_problem* p, Plan* out, bool raw) {
   const size_t esz = pl.arm_f32 ? 4 : 2;
   size_t off = 0;
   pl.off_table = off;
-  off = round_up(off + (pl.varlen ? 2 * sizeof(int32_t) * (size_t)(pl.n_seq + 1) : 0), 256);
+  // packed batch: bounds and chunk prefix ([n_seq + 1] each), then the scan's dispatch order
+  off = round_up(off + (pl.varlen ? sizeof(int32_t) * (3 * (size_t)pl.n_seq + 2) : 0), 256);
   // split composition: T and P of every chunk pass through the workspace
   const size_t tile = pl.fused ? 0 : (size_t)pl.tile_slots * pl.hv * gdn::tile_elems(C) * esz;
   pl.off_T = off;

@@ -73,7 +73,8 @@ struct Params {
   void* o;
   float* hT;
   uint32_t* status;
-  int32_t* table;  // varlen: [n_seq+1] sanitised bounds, then [n_seq+1] chunk prefix
+  int32_t* table;  // varlen: [n_seq+1] sanitised bounds, [n_seq+1] chunk prefix, then
+                   // [n_seq] the scan's dispatch order (longest sequences first)
   void* Tws;       // [slot][hv][tile_elems(C)] solved T fragments (arm element type)
   void* Pws;       // [slot][hv][tile_elems(C)] masked P fragments (arm element type)
   void* Gws;       // per-channel gate: [slot][hv][3][C][dk] e^{G} K, e^{G_C-G} K, e^{G} Q

@@ -349,9 +349,21 @@ __device__ __forceinline__ int64_t store_slot(const Params& p, int64_t slot) {
 }
 
 // ---------------------------------------------------- chunk table --------
+// A bucket of a sequence's chunk count, monotone in it: the count itself below 4, else
+// 4 e + the two bits below the leading one (e = its bit length - 1), so a bucket spans at
+// most a quarter of its lower end.  0 .. 107 for counts below 2^27.
+__device__ __forceinline__ int chunk_bucket(int32_t c) {
+  if (c < 4) return c;
+  const int e = 31 - __clz(c);
+  return min(127, 4 * e + ((c >> (e - 2)) & 3));
+}
+
 // Sanitised bounds b_0 = 0, b_i = min(total, max(0, max_{1<=j<=i} cu_j)), b_n = total,
 // so every index stays inside [0, total] whatever cu_seqlens holds; any difference
-// from the given offsets sets GDN_ST_BAD_SEQLENS.  Then the chunk prefix over sequences.
+// from the given offsets sets GDN_ST_BAD_SEQLENS.  Then the chunk prefix over sequences,
+// and the scan's dispatch order: the sequences by descending chunk bucket (a counting
+// sort over 128 buckets; ties in any order), so that the first round of a packed batch's
+// scan workgroups takes its longest sequences, whatever the order of cu_seqlens.
 __global__ __launch_bounds__(256) void gdn_chunk_table(Params p, int C) {
   __shared__ int32_t sbuf[256];
   __shared__ int32_t carry;
@@ -405,6 +417,25 @@ __global__ __launch_bounds__(256) void gdn_chunk_table(Params p, int C) {
   }
   if (tid == 0) cpre[0] = 0;
   if (bad) atomicOr(p.status, GDN_ST_BAD_SEQLENS);
+  __syncthreads();
+  // dispatch order: bucket histogram, descending start of each bucket, then each
+  // sequence takes the next place of its bucket
+  __shared__ int32_t start[128];
+  int32_t* order = cpre + n + 1;
+  if (tid < 128) start[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) atomicAdd(&start[127 - chunk_bucket(cpre[i + 1] - cpre[i])], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int32_t sum = 0;
+    for (int b = 0; b < 128; ++b) {
+      const int32_t c = start[b];
+      start[b] = sum;
+      sum += c;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) order[atomicAdd(&start[127 - chunk_bucket(cpre[i + 1] - cpre[i])], 1)] = i;
 }
 
 // ------------------------------------------------ 16-byte staging -------
@@ -1574,6 +1605,8 @@ __global__ __launch_bounds__(FUSED ? 384 : 256) void gdn_scan(Params p) {
     h = bid % p.hv;
     n = bid / p.hv;
   }
+  // a packed batch is dispatched longest sequences first (gdn_chunk_table)
+  if (p.varlen) n = p.table[2 * (p.n_seq + 1) + n];
   const int kh = h / (p.hv / p.hk);
 
   // Sequence split: virtual sequence n is part `part` of real sequence nr; kind 0 scans the
