@@ -50,7 +50,7 @@ def log(*a):
 
 
 def algorithmic(spec, chunk):
-    """Algorithmic bytes and flops of the two kernels for one layer (see DESIGN.md).
+    """Algorithmic bytes and flops of the two kernels for one layer.
 
     prep (per chunk and key head, then per value head of the group):
       bytes: q, k chunk rows + g, beta rows + T and P fragments written (bf16)
@@ -777,8 +777,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(see DESIGN.md for how the path would shard)" % args.gpus, file=sys.stderr)
+        print("bench.py: the library runs on one GPU; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
